@@ -1,0 +1,240 @@
+"""Plain, slow, fp64 CPU oracle of the DFlash draft block-attention path.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, ``__graft_entry__.smoke()``
+and the ``cpu_baseline`` leg of ``bench.py``; never by the product path. It
+shares no code, header, table or helper with the HIP library.
+
+Everything is computed in float64 from the exact input values (bf16 or f32
+inputs are widened without change). There is no intermediate rounding, no
+blocking, no fusion and no online softmax: each function is the plain
+definition of its step, written in the order the pages apply the steps.
+
+Sources (pages of the vllm.cpp project):
+  * "qwen3_dflash.cpp" page -- file header (the block attention is the one new
+    operation; full-attention layers are bidirectional inside the block, sliding
+    window layers causal with a window), ``PrecomputeContextKVDevice`` (hidden
+    RMSNorm, K/V projection as rows of the merged qkv weight, per-head k-norm,
+    NeoX RoPE at context positions, V raw), ``ForwardBlockLogits`` and
+    ``ForwardWithCtxKVDev`` (per-head q/k RMSNorm, NeoX RoPE at block positions,
+    scale 1/sqrt(Dh), attention of each block over its request's
+    [context; block] sequence, only block-query rows kept).
+  * "qwen3.cpp" page -- file header (standard, non-gemma RMSNorm; q/k norm
+    applied before RoPE).
+
+Readings taken where the pages are silent (each also listed in the design doc):
+  * GQA: q-head h reads kv-head h // (Hq/Hkv).
+  * NeoX RoPE pairs element i with element i + Dh/2; inverse frequency
+    theta**(-2i/Dh); the whole head dimension rotates.
+  * The mask is defined on the index in the per-request combined sequence
+    [context rows 0..C-1; block rows C..C+B-1], the only thing the pages hand the
+    attention (cumulative sequence lengths). Bidirectional: every key visible.
+    Causal: key k visible to query i iff k <= i; with a window W > 0 also
+    i - k < W (W keys including the query's own row).
+  * A query row with no visible key yields 0 (cannot happen when B >= 1).
+
+Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
+against closed forms, invariants, library routines and brute force. No
+function is "parity unpinned" at the level of its definition; the pairing
+convention of RoPE is fixed only by the name "NeoX" on the pages (see
+the design doc).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "rms_norm",
+    "rope_inv_freq",
+    "rope_neox",
+    "qk_norm_rope",
+    "context_projection",
+    "context_kv",
+    "attention_visibility",
+    "block_attention",
+    "draft_block_attention",
+]
+
+
+def _f64(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def rms_norm(x, w, eps):
+    """Standard RMSNorm over the last axis: ``x * w / sqrt(mean(x**2) + eps)``.
+
+    "qwen3_dflash.cpp" page, ``PrecomputeContextKVDevice`` (hidden_norm and
+    k_norm) and ``ForwardBlockLogits`` (q_norm, k_norm over head_dim), both
+    with the non-gemma flag; "qwen3.cpp" page header (standard RMSNorm, weight
+    multiplies directly, no 1 + w).
+    """
+    x = _f64(x)
+    w = _f64(w)
+    mean_sq = np.mean(x * x, axis=-1, keepdims=True)
+    return x / np.sqrt(mean_sq + float(eps)) * w
+
+
+def rope_inv_freq(head_dim, theta):
+    """Inverse frequencies ``theta ** (-2 i / Dh)`` for i in [0, Dh/2)."""
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return float(theta) ** (-(2.0 * i) / float(head_dim))
+
+
+def rope_neox(x, positions, theta):
+    """NeoX (rotate-half) rotary embedding.
+
+    ``x`` is ``[T, H, Dh]``; ``positions`` is ``[T]`` integer. For each row t
+    and pair index i < Dh/2, with angle a = positions[t] * inv_freq[i]:
+    ``y[i] = x[i] cos a - x[i + Dh/2] sin a`` and
+    ``y[i + Dh/2] = x[i + Dh/2] cos a + x[i] sin a``.
+
+    "qwen3_dflash.cpp" page: ``RopeNeox`` applied to q and k at the block
+    positions (``ForwardBlockLogits``) and to K at the context positions
+    (``PrecomputeContextKVDevice``).
+    """
+    x = _f64(x)
+    t, h, d = x.shape
+    half = d // 2
+    ang = _f64(positions).reshape(t, 1) * rope_inv_freq(d, theta).reshape(1, half)
+    cos = np.cos(ang)[:, None, :]
+    sin = np.sin(ang)[:, None, :]
+    x1 = x[:, :, :half]
+    x2 = x[:, :, half:]
+    return np.concatenate([x1 * cos - x2 * sin, x2 * cos + x1 * sin], axis=-1)
+
+
+def qk_norm_rope(q, k, q_norm_w, k_norm_w, positions, eps, theta):
+    """Per-head RMSNorm of q and k over head_dim, then NeoX RoPE on both.
+
+    ``q`` ``[T, Hq, Dh]`` (or None for the K-only form used on context rows),
+    ``k`` ``[T, Hkv, Dh]``. Returns ``(q_hat or None, k_hat)``.
+
+    "qwen3_dflash.cpp" page, ``ForwardBlockLogits``: q_norm then k_norm then
+    RopeNeox(q, k, positions); "qwen3.cpp" page header: norm before RoPE.
+    """
+    k_hat = rope_neox(rms_norm(k, k_norm_w, eps), positions, theta)
+    if q is None:
+        return None, k_hat
+    q_hat = rope_neox(rms_norm(q, q_norm_w, eps), positions, theta)
+    return q_hat, k_hat
+
+
+def context_projection(hidden, hidden_norm_w, w_k, w_v, eps):
+    """Hidden RMSNorm then the K and V projections of the context rows.
+
+    ``normed = RMSNorm(hidden, hidden_norm_w)``; ``K = normed @ w_k.T`` and
+    ``V = normed @ w_v.T`` where ``w_k``/``w_v`` are ``[Hkv*Dh, H]`` (rows of
+    the merged qkv weight). Returns ``(K_raw [C, Hkv*Dh], V [C, Hkv*Dh])``.
+
+    "qwen3_dflash.cpp" page, ``PrecomputeContextKVDevice``: RmsNorm with
+    hidden_norm, then MatmulBT against the K and V row slices.
+    """
+    normed = rms_norm(hidden, hidden_norm_w, eps)
+    k_raw = normed @ _f64(w_k).T
+    v = normed @ _f64(w_v).T
+    return k_raw, v
+
+
+def context_kv(hidden, hidden_norm_w, w_k, w_v, k_norm_w, positions,
+               num_kv_heads, head_dim, eps, theta):
+    """Context K/V precompute: projection, per-head k-norm, NeoX RoPE on K.
+
+    Returns ``(K_hat [C, Hkv, Dh], V [C, Hkv, Dh])``; V is left raw.
+
+    "qwen3_dflash.cpp" page, ``PrecomputeContextKVDevice`` and the
+    ``ContextKVDev`` record (K normed and rotated, V raw).
+    """
+    k_raw, v = context_projection(hidden, hidden_norm_w, w_k, w_v, eps)
+    c = k_raw.shape[0]
+    k3 = k_raw.reshape(c, num_kv_heads, head_dim)
+    _, k_hat = qk_norm_rope(None, k3, None, k_norm_w, positions, eps, theta)
+    return k_hat, v.reshape(c, num_kv_heads, head_dim)
+
+
+def attention_visibility(ctx_len, blk_len, causal, window):
+    """Boolean ``[blk_len, ctx_len + blk_len]`` visibility of keys to block queries.
+
+    Indices are positions in the per-request combined sequence: context rows
+    0..ctx_len-1, then block rows ctx_len..ctx_len+blk_len-1. Block query b sits
+    at index ctx_len + b. Bidirectional (``causal`` false): all keys visible.
+    Causal: key k visible iff k <= query index; with ``window`` > 0 also
+    ``query index - k < window``.
+
+    "qwen3_dflash.cpp" page header: bidirectional in-block attention on full
+    attention layers, causal plus sliding window on SWA layers; the attention
+    receives only cumulative lengths, so the mask lives on these indices.
+    """
+    n = ctx_len + blk_len
+    vis = np.ones((blk_len, n), dtype=bool)
+    if causal:
+        qi = ctx_len + np.arange(blk_len).reshape(-1, 1)
+        kj = np.arange(n).reshape(1, -1)
+        vis = kj <= qi
+        if window > 0:
+            vis &= (qi - kj) < window
+    elif window > 0:
+        raise ValueError("a sliding window is only defined for causal layers")
+    return vis
+
+
+def block_attention(q, k_blk, v_blk, k_ctx, v_ctx, cu_ctx, cu_blk, scale,
+                    causal=False, window=0):
+    """softmax(scale * Q K^T) V of each block over its [context; block] keys.
+
+    ``q`` ``[T, Hq, Dh]``, ``k_blk``/``v_blk`` ``[T, Hkv, Dh]`` (already normed
+    and rotated for q and k), ``k_ctx``/``v_ctx`` ``[sum C, Hkv, Dh]``;
+    ``cu_ctx``/``cu_blk`` are the ``[R+1]`` cumulative row counts. Returns the
+    block-query outputs ``[T, Hq, Dh]``.
+
+    "qwen3_dflash.cpp" page, ``ForwardWithCtxKVDev``: each request's combined
+    sequence is its context rows followed by its block rows, the attention runs
+    over it with the layer's causal / window flags, and only the block-query
+    rows are kept; scale is 1/sqrt(head_dim).
+    """
+    q = _f64(q)
+    k_blk = _f64(k_blk)
+    v_blk = _f64(v_blk)
+    k_ctx = _f64(k_ctx)
+    v_ctx = _f64(v_ctx)
+    cu_ctx = np.asarray(cu_ctx, dtype=np.int64)
+    cu_blk = np.asarray(cu_blk, dtype=np.int64)
+    t, hq, d = q.shape
+    hkv = k_blk.shape[1]
+    group = hq // hkv
+    out = np.zeros((t, hq, d), dtype=np.float64)
+    for r in range(len(cu_blk) - 1):
+        c0, c1 = cu_ctx[r], cu_ctx[r + 1]
+        b0, b1 = cu_blk[r], cu_blk[r + 1]
+        if b1 == b0:
+            continue
+        keys = np.concatenate([k_ctx[c0:c1], k_blk[b0:b1]], axis=0)
+        vals = np.concatenate([v_ctx[c0:c1], v_blk[b0:b1]], axis=0)
+        vis = attention_visibility(int(c1 - c0), int(b1 - b0), causal, window)
+        for h in range(hq):
+            g = h // group
+            s = scale * (q[b0:b1, h, :] @ keys[:, g, :].T)
+            s = np.where(vis, s, -np.inf)
+            m = np.max(s, axis=1, keepdims=True)
+            m = np.where(np.isfinite(m), m, 0.0)
+            e = np.where(vis, np.exp(s - m), 0.0)
+            denom = e.sum(axis=1, keepdims=True)
+            num = e @ vals[:, g, :]
+            out[b0:b1, h, :] = np.where(denom > 0, num / np.where(denom > 0, denom, 1.0), 0.0)
+    return out
+
+
+def draft_block_attention(q, k_blk, v_blk, blk_positions, k_ctx_hat, v_ctx,
+                          cu_ctx, cu_blk, q_norm_w, k_norm_w, eps, theta,
+                          scale, causal=False, window=0):
+    """The whole draft-side path for one layer: q/k norm -> RoPE -> attention.
+
+    Block q and k are raw projections; the context keys ``k_ctx_hat`` are
+    already normed and rotated (the output of ``context_kv`` or of the K-only
+    ``qk_norm_rope``). Returns ``(out, q_hat, k_blk_hat)``.
+
+    "qwen3_dflash.cpp" page, ``ForwardWithCtxKVDev``: q/k RMSNorm, RopeNeox,
+    then block attention over [context; block].
+    """
+    q_hat, k_hat = qk_norm_rope(q, k_blk, q_norm_w, k_norm_w, blk_positions, eps, theta)
+    out = block_attention(q_hat, k_hat, v_blk, k_ctx_hat, v_ctx, cu_ctx, cu_blk,
+                          scale, causal, window)
+    return out, q_hat, k_hat

@@ -1,0 +1,503 @@
+"""Pins of the fp64 oracle to things other than itself (CPU only).
+
+Each pin checks the oracle against a closed form, an invariant the mathematics
+fixes, an independent library routine (torch fp64 CPU ops) or a brute-force
+second formulation on tiny inputs. ``test_pins_catch_planted_mistakes`` plants
+plausible mistakes in the oracle (a dropped term, a wrong sign, a wrong index,
+a transposed operand) and checks that some pin fails for each.
+
+The pages print no worked numeric example, so there are no printed values to
+pin against (no fixture under tests/golden/ comes from the pages).
+"""
+import math
+import types
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import dflash_oracle as O
+
+RNG = np.random.default_rng(12345)
+
+
+def _ns(**over):
+    """The oracle's functions as a namespace, optionally with some replaced."""
+    base = dict(
+        rms_norm=O.rms_norm,
+        rope_neox=O.rope_neox,
+        qk_norm_rope=O.qk_norm_rope,
+        context_projection=O.context_projection,
+        context_kv=O.context_kv,
+        attention_visibility=O.attention_visibility,
+        block_attention=O.block_attention,
+    )
+    base.update(over)
+    return types.SimpleNamespace(**base)
+
+
+# ----------------------------------------------------------------------------- RMSNorm pins
+
+def pin_rms_norm_library(X):
+    x = RNG.standard_normal((7, 33))
+    w = RNG.uniform(0.5, 1.5, 33)
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x), (33,), torch.from_numpy(w), eps=1e-6)
+    np.testing.assert_allclose(X.rms_norm(x, w, 1e-6), ref.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def pin_rms_norm_closed_form(X):
+    # Unit weight: the output's mean square is ms / (ms + eps) exactly.
+    x = RNG.standard_normal((5, 64)) * 0.01
+    eps = 1e-4
+    y = X.rms_norm(x, np.ones(64), eps)
+    ms = np.mean(x * x, axis=1)
+    np.testing.assert_allclose(np.mean(y * y, axis=1), ms / (ms + eps), rtol=1e-12)
+    # Weight multiplies element-wise; a single constant row c gives c / sqrt(c^2 + eps).
+    c = 0.3
+    y = X.rms_norm(np.full((1, 4), c), np.array([1.0, 2.0, 0.5, 1.0]), 1e-2)
+    np.testing.assert_allclose(y[0], np.array([1.0, 2.0, 0.5, 1.0]) * c / math.sqrt(c * c + 1e-2),
+                               rtol=1e-14)
+
+
+# ----------------------------------------------------------------------------- RoPE pins
+
+def pin_rope_complex_form(X):
+    # NeoX rotate-half == complex multiply of (x_i + i x_{i+D/2}) by exp(i p f_i).
+    t, h, d, theta = 6, 3, 16, 1e4
+    x = RNG.standard_normal((t, h, d))
+    pos = RNG.integers(0, 5000, t)
+    f = theta ** (-np.arange(d // 2) * 2.0 / d)
+    z = (x[..., : d // 2] + 1j * x[..., d // 2:]) * np.exp(1j * pos[:, None, None] * f[None, None, :])
+    ref = np.concatenate([z.real, z.imag], axis=-1)
+    np.testing.assert_allclose(X.rope_neox(x, pos, theta), ref, rtol=1e-12, atol=1e-12)
+
+
+def pin_rope_hand_case(X):
+    # Dh = 4, theta = 100: inverse frequencies 1 and 0.1; position 3.
+    x = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    y = X.rope_neox(x, np.array([3]), 100.0)[0, 0]
+    a0, a1 = 3.0, 0.3
+    ref = [1 * math.cos(a0) - 3 * math.sin(a0), 2 * math.cos(a1) - 4 * math.sin(a1),
+           3 * math.cos(a0) + 1 * math.sin(a0), 4 * math.cos(a1) + 2 * math.sin(a1)]
+    np.testing.assert_allclose(y, ref, rtol=1e-14, atol=1e-14)
+
+
+def pin_rope_invariants(X):
+    t, d, theta = 9, 64, 1e6
+    x = RNG.standard_normal((t, 2, d))
+    # position 0 is the identity
+    np.testing.assert_allclose(X.rope_neox(x, np.zeros(t, int), theta), x, rtol=0, atol=0)
+    # norm preserved
+    pos = RNG.integers(0, 40000, t)
+    y = X.rope_neox(x, pos, theta)
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), np.linalg.norm(x, axis=-1), rtol=1e-13)
+    # <R(q,p), R(k,p')> depends only on p - p'
+    q = RNG.standard_normal((1, 1, d))
+    k = RNG.standard_normal((1, 1, d))
+    dots = []
+    for p in (0, 17, 1000, 33000):
+        rq = X.rope_neox(q, np.array([p + 5]), theta)
+        rk = X.rope_neox(k, np.array([p]), theta)
+        dots.append(float(np.sum(rq * rk)))
+    np.testing.assert_allclose(dots, dots[0], rtol=1e-9)
+    # element 0 pairs with element Dh/2 (rotate-half), nothing else moves
+    e = np.zeros((1, 1, d))
+    e[0, 0, 0] = 1.0
+    y = X.rope_neox(e, np.array([7]), theta)[0, 0]
+    nz = np.flatnonzero(np.abs(y) > 1e-15)
+    assert nz.tolist() == [0, d // 2]
+    np.testing.assert_allclose([y[0], y[d // 2]], [math.cos(7.0), math.sin(7.0)], rtol=1e-14)
+
+
+def pin_qk_norm_then_rope(X):
+    # norm first, rope second: with unit weights the rotated head keeps the
+    # normed RMS; q and k rows use the same positions.
+    t, d = 5, 32
+    q = RNG.standard_normal((t, 4, d)) * 3.0
+    k = RNG.standard_normal((t, 2, d)) * 0.2
+    pos = np.arange(t) * 11
+    wq = RNG.uniform(0.5, 1.5, d)
+    wk = RNG.uniform(0.5, 1.5, d)
+    qh, kh = X.qk_norm_rope(q, k, wq, wk, pos, 1e-6, 1e6)
+    ref_q = X.rope_neox(torch.nn.functional.rms_norm(torch.from_numpy(q), (d,),
+                                                     torch.from_numpy(wq), eps=1e-6).numpy(), pos, 1e6)
+    np.testing.assert_allclose(qh, ref_q, rtol=1e-12, atol=1e-12)
+    qu, ku = X.qk_norm_rope(q, k, np.ones(d), np.ones(d), pos, 0.0, 1e6)
+    np.testing.assert_allclose(np.mean(ku * ku, axis=-1), 1.0, rtol=1e-12)
+    np.testing.assert_allclose(np.mean(qu * qu, axis=-1), 1.0, rtol=1e-12)
+    none_q, k_only = X.qk_norm_rope(None, k, None, wk, pos, 1e-6, 1e6)
+    assert none_q is None
+    np.testing.assert_allclose(k_only, kh, rtol=0, atol=0)
+
+
+# ----------------------------------------------------------------------------- projection pins
+
+def pin_projection_library(X):
+    c, hsz, kdim = 9, 48, 16
+    h = RNG.standard_normal((c, hsz))
+    wn = RNG.uniform(0.5, 1.5, hsz)
+    wk = RNG.standard_normal((kdim, hsz)) * 0.02
+    wv = RNG.standard_normal((kdim, hsz)) * 0.02
+    kr, v = X.context_projection(h, wn, wk, wv, 1e-6)
+    th = torch.nn.functional.rms_norm(torch.from_numpy(h), (hsz,), torch.from_numpy(wn), eps=1e-6)
+    np.testing.assert_allclose(kr, torch.nn.functional.linear(th, torch.from_numpy(wk)).numpy(),
+                               rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(v, torch.nn.functional.linear(th, torch.from_numpy(wv)).numpy(),
+                               rtol=1e-12, atol=1e-14)
+
+
+def pin_context_kv_structure(X):
+    # chunked == whole (rows are independent), V raw, K normed then rotated per head.
+    c, hsz, hkv, d = 12, 40, 2, 8
+    h = RNG.standard_normal((c, hsz))
+    wn = RNG.uniform(0.5, 1.5, hsz)
+    wk = RNG.standard_normal((hkv * d, hsz)) * 0.02
+    wv = RNG.standard_normal((hkv * d, hsz)) * 0.02
+    wkn = RNG.uniform(0.5, 1.5, d)
+    pos = np.arange(c)
+    k, v = X.context_kv(h, wn, wk, wv, wkn, pos, hkv, d, 1e-6, 1e6)
+    k1, v1 = X.context_kv(h[:5], wn, wk, wv, wkn, pos[:5], hkv, d, 1e-6, 1e6)
+    k2, v2 = X.context_kv(h[5:], wn, wk, wv, wkn, pos[5:], hkv, d, 1e-6, 1e6)
+    np.testing.assert_allclose(np.concatenate([k1, k2]), k, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(np.concatenate([v1, v2]), v, rtol=1e-13, atol=1e-15)
+    # torch composition of the same steps
+    th = torch.nn.functional.rms_norm(torch.from_numpy(h), (hsz,), torch.from_numpy(wn), eps=1e-6)
+    tk = torch.nn.functional.linear(th, torch.from_numpy(wk)).reshape(c, hkv, d)
+    tv = torch.nn.functional.linear(th, torch.from_numpy(wv)).reshape(c, hkv, d)
+    tkn = torch.nn.functional.rms_norm(tk, (d,), torch.from_numpy(wkn), eps=1e-6).numpy()
+    f = 1e6 ** (-np.arange(d // 2) * 2.0 / d)
+    z = (tkn[..., : d // 2] + 1j * tkn[..., d // 2:]) * np.exp(1j * pos[:, None, None] * f)
+    np.testing.assert_allclose(k, np.concatenate([z.real, z.imag], -1), rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(v, tv.numpy(), rtol=1e-12, atol=1e-15)
+    # V per head in order: head g of V is rows g*d..(g+1)*d of the V weight.
+    np.testing.assert_allclose(v[:, 1, :], (th.numpy() @ wv[d:2 * d].T), rtol=1e-12, atol=1e-15)
+
+
+# ----------------------------------------------------------------------------- attention pins
+
+def _rand_batch(ctx_lens, blk_lens, hq, hkv, d, seed):
+    rng = np.random.default_rng(seed)
+    cu_c = np.concatenate([[0], np.cumsum(ctx_lens)]).astype(np.int64)
+    cu_b = np.concatenate([[0], np.cumsum(blk_lens)]).astype(np.int64)
+    q = rng.standard_normal((cu_b[-1], hq, d))
+    kb = rng.standard_normal((cu_b[-1], hkv, d))
+    vb = rng.standard_normal((cu_b[-1], hkv, d))
+    kc = rng.standard_normal((cu_c[-1], hkv, d))
+    vc = rng.standard_normal((cu_c[-1], hkv, d))
+    return q, kb, vb, kc, vc, cu_c, cu_b
+
+
+def _brute(q, kb, vb, kc, vc, cu_c, cu_b, scale, causal, window):
+    """Second formulation: explicit loops, explicit mask test, exp without max shift."""
+    t, hq, d = q.shape
+    hkv = kb.shape[1]
+    out = np.zeros_like(q)
+    for r in range(len(cu_b) - 1):
+        cl = int(cu_c[r + 1] - cu_c[r])
+        for b in range(int(cu_b[r + 1] - cu_b[r])):
+            row = int(cu_b[r]) + b
+            qi = cl + b  # index of this query in [context; block]
+            for h in range(hq):
+                g = h * hkv // hq
+                ws, acc = [], [[] for _ in range(d)]
+                for j in range(cl + int(cu_b[r + 1] - cu_b[r])):
+                    if causal and (j > qi or (window > 0 and qi - j >= window)):
+                        continue
+                    kr = kc[int(cu_c[r]) + j, g] if j < cl else kb[int(cu_b[r]) + j - cl, g]
+                    vr = vc[int(cu_c[r]) + j, g] if j < cl else vb[int(cu_b[r]) + j - cl, g]
+                    s = math.fsum(float(a) * float(c) for a, c in zip(q[row, h], kr)) * scale
+                    e = math.exp(s)
+                    ws.append(e)
+                    for i in range(d):
+                        acc[i].append(e * float(vr[i]))
+                z = math.fsum(ws)
+                for i in range(d):
+                    out[row, h, i] = math.fsum(acc[i]) / z
+    return out
+
+
+def pin_attention_brute_force(X):
+    for causal, window in ((False, 0), (True, 0), (True, 5)):
+        args = _rand_batch([7, 0, 12], [4, 3, 2], 4, 2, 8, 7)
+        s = 1 / math.sqrt(8)
+        got = X.block_attention(*args, s, causal, window)
+        ref = _brute(*args, s, causal, window)
+        np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-13)
+
+
+def pin_attention_library(X):
+    # torch SDPA (fp64, CPU, explicit boolean mask, GQA by repeated kv heads).
+    q, kb, vb, kc, vc, cu_c, cu_b = _rand_batch([30, 3], [6, 5], 8, 2, 16, 8)
+    for causal, window in ((False, 0), (True, 0), (True, 9)):
+        got = X.block_attention(q, kb, vb, kc, vc, cu_c, cu_b, 0.37, causal, window)
+        for r in range(2):
+            c0, c1, b0, b1 = cu_c[r], cu_c[r + 1], cu_b[r], cu_b[r + 1]
+            n, bl = c1 - c0 + b1 - b0, b1 - b0
+            keys = torch.from_numpy(np.concatenate([kc[c0:c1], kb[b0:b1]])).permute(1, 0, 2)
+            vals = torch.from_numpy(np.concatenate([vc[c0:c1], vb[b0:b1]])).permute(1, 0, 2)
+            qq = torch.from_numpy(q[b0:b1]).permute(1, 0, 2)
+            qi = torch.arange(bl).reshape(-1, 1) + (c1 - c0)
+            kj = torch.arange(n).reshape(1, -1)
+            mask = torch.ones(bl, n, dtype=torch.bool)
+            if causal:
+                mask = kj <= qi
+                if window > 0:
+                    mask &= (qi - kj) < window
+            ref = torch.nn.functional.scaled_dot_product_attention(
+                qq, keys.contiguous(), vals.contiguous(), attn_mask=mask, scale=0.37,
+                enable_gqa=True)
+            np.testing.assert_allclose(got[b0:b1], ref.permute(1, 0, 2).numpy(), rtol=1e-11, atol=1e-12)
+
+
+def pin_attention_closed_forms(X):
+    q, kb, vb, kc, vc, cu_c, cu_b = _rand_batch([10, 4], [5, 3], 4, 2, 8, 9)
+    # softmax rows sum to one: V == 1 gives output 1.
+    got = X.block_attention(q, kb, np.ones_like(vb), kc, np.ones_like(vc), cu_c, cu_b, 0.5)
+    np.testing.assert_allclose(got, 1.0, rtol=0, atol=1e-14)
+    # one visible key (causal, window 1): output is the row's own V.
+    got = X.block_attention(q, kb, vb, kc, vc, cu_c, cu_b, 0.5, True, 1)
+    g = np.arange(4) * 2 // 4
+    np.testing.assert_allclose(got, vb[:, g, :], rtol=0, atol=0)
+    # empty context, one block row: output is that row's V.
+    a = _rand_batch([0], [1], 4, 2, 8, 3)
+    got = X.block_attention(*a, 0.9)
+    np.testing.assert_allclose(got[0], a[2][0, g, :], rtol=0, atol=0)
+    # all keys equal: output is the plain mean of the visible values.
+    kc2 = np.broadcast_to(kc[:1], kc.shape).copy()
+    kb2 = np.broadcast_to(kc[:1], kb.shape).copy()
+    got = X.block_attention(q, kb2, vb, kc2, vc, cu_c, cu_b, 0.5)
+    for r in range(2):
+        vals = np.concatenate([vc[cu_c[r]:cu_c[r + 1]], vb[cu_b[r]:cu_b[r + 1]]])
+        np.testing.assert_allclose(got[cu_b[r]:cu_b[r + 1]],
+                                   np.broadcast_to(vals.mean(0)[g], got[cu_b[r]:cu_b[r + 1]].shape),
+                                   rtol=1e-13, atol=1e-14)
+    # causal, query b of a request sees C + b + 1 keys: with equal keys the
+    # output is the mean of exactly those.
+    got = X.block_attention(q, kb2, vb, kc2, vc, cu_c, cu_b, 0.5, True, 0)
+    vals = np.concatenate([vc[0:10], vb[0:5]])
+    for b in range(5):
+        np.testing.assert_allclose(got[b], vals[: 10 + b + 1].mean(0)[g], rtol=1e-13, atol=1e-14)
+    # window W >= C + B reduces to plain causal.
+    np.testing.assert_allclose(X.block_attention(q, kb, vb, kc, vc, cu_c, cu_b, 0.5, True, 100),
+                               X.block_attention(q, kb, vb, kc, vc, cu_c, cu_b, 0.5, True, 0),
+                               rtol=0, atol=0)
+
+
+def pin_attention_permutations(X):
+    q, kb, vb, kc, vc, cu_c, cu_b = _rand_batch([9], [6], 4, 2, 8, 10)
+    base = X.block_attention(q, kb, vb, kc, vc, cu_c, cu_b, 0.4)
+    # block-query permutation equivariance (bidirectional)
+    p = np.array([3, 0, 5, 1, 4, 2])
+    np.testing.assert_allclose(X.block_attention(q[p], kb, vb, kc, vc, cu_c, cu_b, 0.4), base[p],
+                               rtol=1e-13, atol=1e-14)
+    # joint permutation of block (K, V) pairs, and of context pairs
+    np.testing.assert_allclose(X.block_attention(q, kb[p], vb[p], kc, vc, cu_c, cu_b, 0.4), base,
+                               rtol=1e-13, atol=1e-14)
+    pc = RNG.permutation(9)
+    np.testing.assert_allclose(X.block_attention(q, kb, vb, kc[pc], vc[pc], cu_c, cu_b, 0.4), base,
+                               rtol=1e-13, atol=1e-14)
+    # GQA: q-head h reads kv-head h // (Hq/Hkv)
+    for h in range(4):
+        g = h // 2
+        one = X.block_attention(q[:, h:h + 1], kb[:, g:g + 1], vb[:, g:g + 1], kc[:, g:g + 1],
+                                vc[:, g:g + 1], cu_c, cu_b, 0.4)
+        np.testing.assert_allclose(base[:, h:h + 1], one, rtol=0, atol=0)
+    # scale -> 0: mean of all values
+    got = X.block_attention(q, kb, vb, kc, vc, cu_c, cu_b, 0.0)
+    np.testing.assert_allclose(got, np.broadcast_to(np.concatenate([vc, vb]).mean(0)[[0, 0, 1, 1]],
+                                                    got.shape), rtol=1e-13, atol=1e-14)
+
+
+def pin_requests_independent(X):
+    # A packed batch equals each request run alone.
+    q, kb, vb, kc, vc, cu_c, cu_b = _rand_batch([5, 11, 0], [3, 4, 2], 4, 2, 8, 11)
+    got = X.block_attention(q, kb, vb, kc, vc, cu_c, cu_b, 0.6, True, 6)
+    for r in range(3):
+        c0, c1, b0, b1 = cu_c[r], cu_c[r + 1], cu_b[r], cu_b[r + 1]
+        one = X.block_attention(q[b0:b1], kb[b0:b1], vb[b0:b1], kc[c0:c1], vc[c0:c1],
+                                [0, c1 - c0], [0, b1 - b0], 0.6, True, 6)
+        np.testing.assert_allclose(got[b0:b1], one, rtol=0, atol=0)
+
+
+def pin_visibility(X):
+    v = X.attention_visibility(4, 3, True, 3)
+    ref = np.array([[0, 0, 1, 1, 1, 0, 0],
+                    [0, 0, 0, 1, 1, 1, 0],
+                    [0, 0, 0, 0, 1, 1, 1]], dtype=bool)
+    assert (v == ref).all()
+    assert X.attention_visibility(4, 3, False, 0).all()
+    with pytest.raises(ValueError):
+        X.attention_visibility(4, 3, False, 2)
+
+
+PINS = [
+    pin_rms_norm_library, pin_rms_norm_closed_form, pin_rope_complex_form, pin_rope_hand_case,
+    pin_rope_invariants, pin_qk_norm_then_rope, pin_projection_library, pin_context_kv_structure,
+    pin_attention_brute_force, pin_attention_library, pin_attention_closed_forms,
+    pin_attention_permutations, pin_requests_independent, pin_visibility,
+]
+
+
+@pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
+def test_oracle_pin(pin):
+    pin(_ns())
+
+
+# ----------------------------------------------------------------------------- planted mistakes
+
+def _mut_rms_no_eps(x, w, eps):
+    return O.rms_norm(x, w, 0.0)
+
+
+def _mut_rms_gemma(x, w, eps):
+    return O.rms_norm(x, 1.0 + np.asarray(w), eps)
+
+
+def _mut_rms_sum(x, w, eps):
+    return O.rms_norm(x, w, eps) / math.sqrt(np.asarray(x).shape[-1])
+
+
+def _mut_rope_sign(x, pos, theta):
+    return O.rope_neox(x, -np.asarray(pos), theta)
+
+
+def _mut_rope_interleaved(x, pos, theta):
+    x = np.asarray(x, np.float64)
+    d = x.shape[-1]
+    perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+    inv = np.argsort(perm)
+    return O.rope_neox(x[..., perm], pos, theta)[..., inv]
+
+
+def _mut_rope_freq(x, pos, theta):
+    return O.rope_neox(x, pos, theta ** 0.5)
+
+
+def _mut_qk_order(q, k, wq, wk, pos, eps, theta):
+    kh = O.rms_norm(O.rope_neox(k, pos, theta), wk, eps)
+    if q is None:
+        return None, kh
+    return O.rms_norm(O.rope_neox(q, pos, theta), wq, eps), kh
+
+
+def _mut_attn_gqa_mod(q, kb, vb, kc, vc, cu_c, cu_b, scale, causal=False, window=0):
+    # q-head h reads kv-head h % Hkv instead of h // (Hq/Hkv)
+    q = np.asarray(q)
+    hkv = np.shape(kb)[1]
+    out = np.empty(q.shape)
+    for h in range(q.shape[1]):
+        g = h % hkv
+        out[:, h:h + 1] = O.block_attention(q[:, h:h + 1], kb[:, g:g + 1], vb[:, g:g + 1],
+                                            kc[:, g:g + 1], vc[:, g:g + 1], cu_c, cu_b, scale,
+                                            causal, window)
+    return out
+
+
+def _mut_attn_swap_kv(q, kb, vb, kc, vc, cu_c, cu_b, scale, causal=False, window=0):
+    return O.block_attention(q, vb, kb, vc, kc, cu_c, cu_b, scale, causal, window)
+
+
+def _vis_off_by_one(ctx_len, blk_len, causal, window):
+    n = ctx_len + blk_len
+    vis = np.ones((blk_len, n), dtype=bool)
+    if causal:
+        qi = ctx_len + np.arange(blk_len).reshape(-1, 1)
+        kj = np.arange(n).reshape(1, -1)
+        vis = kj < qi + (qi == ctx_len)  # drops the diagonal except for the first row
+        if window > 0:
+            vis &= (qi - kj) <= window
+    return vis
+
+
+def _vis_window_inclusive(ctx_len, blk_len, causal, window):
+    n = ctx_len + blk_len
+    vis = np.ones((blk_len, n), dtype=bool)
+    if causal:
+        qi = ctx_len + np.arange(blk_len).reshape(-1, 1)
+        kj = np.arange(n).reshape(1, -1)
+        vis = kj <= qi
+        if window > 0:
+            vis &= (qi - kj) <= window
+    return vis
+
+
+def _mut_attn_no_scale(q, kb, vb, kc, vc, cu_c, cu_b, scale, causal=False, window=0):
+    return O.block_attention(q, kb, vb, kc, vc, cu_c, cu_b, 1.0 if scale != 0 else 0.0, causal, window)
+
+
+def _mut_proj_wk_for_v(h, wn, wk, wv, eps):
+    k, _ = O.context_projection(h, wn, wk, wv, eps)
+    return k, O.context_projection(h, wn, wk, wk, eps)[1]
+
+
+def _mut_proj_no_hidden_norm(h, wn, wk, wv, eps):
+    return O.context_projection(h, np.ones_like(np.asarray(wn)), wk, wv, eps)
+
+
+MUTANTS = {
+    "rms_no_eps": dict(rms_norm=_mut_rms_no_eps),
+    "rms_gemma_weight": dict(rms_norm=_mut_rms_gemma),
+    "rms_sum_not_mean": dict(rms_norm=_mut_rms_sum),
+    "rope_sign": dict(rope_neox=_mut_rope_sign),
+    "rope_interleaved_pairs": dict(rope_neox=_mut_rope_interleaved),
+    "rope_wrong_freq": dict(rope_neox=_mut_rope_freq),
+    "qk_rope_before_norm": dict(qk_norm_rope=_mut_qk_order),
+    "attn_gqa_modulo": dict(block_attention=_mut_attn_gqa_mod),
+    "attn_k_v_swapped": dict(block_attention=_mut_attn_swap_kv),
+    "attn_no_scale": dict(block_attention=_mut_attn_no_scale),
+    "proj_v_uses_wk": dict(context_projection=_mut_proj_wk_for_v),
+    "proj_no_hidden_norm_weight": dict(context_projection=_mut_proj_no_hidden_norm),
+}
+
+INTERNAL_MUTANTS = {
+    "mask_off_by_one": _vis_off_by_one,
+    "window_inclusive": _vis_window_inclusive,
+}
+
+
+def _some_pin_fails(ns):
+    for pin in PINS:
+        try:
+            pin(ns)
+        except (AssertionError, ValueError):
+            return pin.__name__
+    return None
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistakes(name):
+    ns = _ns(**MUTANTS[name])
+    # the composite functions route through the mutated pieces too
+    if "rms_norm" in MUTANTS[name] or "rope_neox" in MUTANTS[name]:
+        ns.qk_norm_rope = lambda q, k, wq, wk, pos, eps, th: _compose_qk(ns, q, k, wq, wk, pos, eps, th)
+    if "context_projection" in MUTANTS[name]:
+        ns.context_kv = lambda *a: _compose_ckv(ns, *a)
+    assert _some_pin_fails(ns) is not None, f"no pin detects mutant {name}"
+
+
+@pytest.mark.parametrize("name", sorted(INTERNAL_MUTANTS))
+def test_pins_catch_planted_mask_mistakes(name, monkeypatch):
+    monkeypatch.setattr(O, "attention_visibility", INTERNAL_MUTANTS[name])
+    ns = _ns(attention_visibility=INTERNAL_MUTANTS[name])
+    assert _some_pin_fails(ns) is not None, f"no pin detects mutant {name}"
+
+
+def _compose_qk(ns, q, k, wq, wk, pos, eps, theta):
+    kh = ns.rope_neox(ns.rms_norm(k, wk, eps), pos, theta)
+    if q is None:
+        return None, kh
+    return ns.rope_neox(ns.rms_norm(q, wq, eps), pos, theta), kh
+
+
+def _compose_ckv(ns, h, wn, wk, wv, wkn, pos, hkv, d, eps, theta):
+    kr, v = ns.context_projection(h, wn, wk, wv, eps)
+    c = kr.shape[0]
+    _, kh = ns.qk_norm_rope(None, kr.reshape(c, hkv, d), None, wkn, pos, eps, theta)
+    return kh, v.reshape(c, hkv, d)
+
+
+def test_oracle_package_exports():
+    for name in ("rms_norm", "rope_neox", "qk_norm_rope", "context_kv", "block_attention",
+                 "draft_block_attention"):
+        assert callable(getattr(oracle, name))
