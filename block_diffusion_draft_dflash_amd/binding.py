@@ -1,0 +1,211 @@
+"""Thin ctypes binding of libdflash (include/dflash.h).
+
+Functions carry the C names and only marshal arguments: torch tensors become
+device pointers and sizes, the stream is torch's current HIP stream. Every
+step runs in the library's HIP kernels; there is no fallback. If the library
+is missing, ``load()`` raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdflash.so")
+
+DFLASH_OK = 0
+DFLASH_ERR_INVALID_ARG = -1
+DFLASH_ERR_UNSUPPORTED = -2
+DFLASH_ERR_WORKSPACE = -3
+DFLASH_ERR_HIP = -4
+DFLASH_F32 = 0
+DFLASH_BF16 = 1
+
+# Every symbol include/dflash.h declares.
+EXPORTED = (
+    "dflash_last_error",
+    "dflash_abi_version",
+    "dflash_rope_table",
+    "dflash_qk_norm_rope",
+    "dflash_block_attention_workspace_size",
+    "dflash_block_attention_check",
+    "dflash_block_attention",
+    "dflash_context_kv_workspace_size",
+    "dflash_context_kv",
+)
+
+
+class DflashError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"dflash status {status}: {msg}")
+        self.status = status
+
+
+class BlockAttnParams(ctypes.Structure):
+    """Mirror of ``dflash_block_attn_params``."""
+
+    _fields_ = [
+        ("num_reqs", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+        ("total_ctx", ctypes.c_int64),
+        ("total_blk", ctypes.c_int64),
+        ("max_blk_len", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("causal", ctypes.c_int32),
+        ("window", ctypes.c_int32),
+        ("split_keys", ctypes.c_int32),
+    ]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libdflash and declare its signatures (idempotent)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"{path} is missing: build it with `python -m block_diffusion_draft_dflash_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, I32, I64, F, D, SZ = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_double, ctypes.c_size_t)
+    lib.dflash_last_error.restype = ctypes.c_char_p
+    lib.dflash_last_error.argtypes = []
+    lib.dflash_abi_version.restype = ctypes.c_int
+    lib.dflash_abi_version.argtypes = []
+    lib.dflash_rope_table.restype = ctypes.c_int
+    lib.dflash_rope_table.argtypes = [P, I32, I32, D, P]
+    lib.dflash_qk_norm_rope.restype = ctypes.c_int
+    lib.dflash_qk_norm_rope.argtypes = [ctypes.c_int, P, P, P, P, P, I64, I32, I32, I32, F, P, I32, P]
+    lib.dflash_block_attention_workspace_size.restype = SZ
+    lib.dflash_block_attention_workspace_size.argtypes = [ctypes.POINTER(BlockAttnParams)]
+    lib.dflash_block_attention_check.restype = ctypes.c_int
+    lib.dflash_block_attention_check.argtypes = [ctypes.POINTER(BlockAttnParams)]
+    lib.dflash_block_attention.restype = ctypes.c_int
+    lib.dflash_block_attention.argtypes = [ctypes.POINTER(BlockAttnParams), P, P, P, P, P, P, P, P,
+                                           P, SZ, P]
+    lib.dflash_context_kv_workspace_size.restype = SZ
+    lib.dflash_context_kv_workspace_size.argtypes = [I64, I32, I32, I32]
+    lib.dflash_context_kv.restype = ctypes.c_int
+    lib.dflash_context_kv.argtypes = [P, P, P, P, P, P, I64, I32, I32, I32, F, P, I32, P, P, P, SZ, P]
+    _lib = lib
+    return lib
+
+
+def _check(status: int) -> None:
+    if status != DFLASH_OK:
+        raise DflashError(status, _lib.dflash_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if t.device.type != "cuda":
+        raise ValueError("libdflash takes device tensors")
+    if not t.is_contiguous():
+        raise ValueError("libdflash takes contiguous tensors")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return DFLASH_BF16
+    if t.dtype == torch.float32:
+        return DFLASH_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def dflash_last_error() -> str:
+    return load().dflash_last_error().decode()
+
+
+def dflash_abi_version() -> int:
+    return load().dflash_abi_version()
+
+
+def dflash_rope_table(table: torch.Tensor, max_pos: int, head_dim: int, theta: float,
+                      stream=None) -> None:
+    """Fill ``table`` (f32, [max_pos, head_dim/2, 2]) with the RoPE cos/sin cache."""
+    lib = load()
+    _check(lib.dflash_rope_table(_ptr(table), max_pos, head_dim, float(theta), _stream(stream)))
+
+
+def dflash_qk_norm_rope(q: Optional[torch.Tensor], k: torch.Tensor,
+                        q_norm_w: Optional[torch.Tensor], k_norm_w: torch.Tensor,
+                        positions: torch.Tensor, eps: float, rope_table: torch.Tensor,
+                        stream=None) -> None:
+    """In-place q/k RMSNorm + NeoX RoPE. q ``[T, Hq, Dh]`` (or None), k ``[T, Hkv, Dh]``."""
+    lib = load()
+    t, hkv, dh = k.shape
+    hq = q.shape[1] if q is not None else 0
+    max_pos = rope_table.shape[0]
+    _check(lib.dflash_qk_norm_rope(_dtype_code(k), _ptr(q), _ptr(k), _ptr(q_norm_w),
+                                   _ptr(k_norm_w), _ptr(positions), t, hq, hkv, dh, float(eps),
+                                   _ptr(rope_table), max_pos, _stream(stream)))
+
+
+def make_block_attn_params(num_reqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                           dtype: int, total_ctx: int, total_blk: int, max_blk_len: int,
+                           scale: float, causal: bool = False, window: int = 0,
+                           split_keys: int = 0) -> BlockAttnParams:
+    return BlockAttnParams(num_reqs, num_q_heads, num_kv_heads, head_dim, dtype, total_ctx,
+                           total_blk, max_blk_len, scale, int(bool(causal)), window, split_keys)
+
+
+def dflash_block_attention_check(p: BlockAttnParams) -> int:
+    return load().dflash_block_attention_check(ctypes.byref(p))
+
+
+def dflash_block_attention_workspace_size(p: BlockAttnParams) -> int:
+    return load().dflash_block_attention_workspace_size(ctypes.byref(p))
+
+
+def dflash_block_attention(p: BlockAttnParams, cu_ctx_lens: torch.Tensor,
+                           cu_blk_lens: torch.Tensor, q: torch.Tensor, k_blk: torch.Tensor,
+                           v_blk: torch.Tensor, k_ctx: Optional[torch.Tensor],
+                           v_ctx: Optional[torch.Tensor], out: torch.Tensor,
+                           workspace: Optional[torch.Tensor], stream=None) -> None:
+    lib = load()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dflash_block_attention(ctypes.byref(p), _ptr(cu_ctx_lens), _ptr(cu_blk_lens),
+                                      _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_ctx), _ptr(v_ctx),
+                                      _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dflash_context_kv_workspace_size(T: int, hidden_size: int, num_kv_heads: int,
+                                     head_dim: int) -> int:
+    return load().dflash_context_kv_workspace_size(T, hidden_size, num_kv_heads, head_dim)
+
+
+def dflash_context_kv(hidden: torch.Tensor, hidden_norm_w: torch.Tensor, w_k: torch.Tensor,
+                      w_v: torch.Tensor, k_norm_w: torch.Tensor, positions: torch.Tensor,
+                      num_kv_heads: int, head_dim: int, eps: float, rope_table: torch.Tensor,
+                      k_out: torch.Tensor, v_out: torch.Tensor, workspace: torch.Tensor,
+                      stream=None) -> None:
+    lib = load()
+    t, h = hidden.shape
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check(lib.dflash_context_kv(_ptr(hidden), _ptr(hidden_norm_w), _ptr(w_k), _ptr(w_v),
+                                 _ptr(k_norm_w), _ptr(positions), t, h, num_kv_heads, head_dim,
+                                 float(eps), _ptr(rope_table), rope_table.shape[0], _ptr(k_out),
+                                 _ptr(v_out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def alloc_workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
+    """A zero-filled, 256-byte aligned workspace of at least ``nbytes`` bytes."""
+    if nbytes == 0:
+        return None
+    return torch.zeros((nbytes + 255) // 256 * 256, dtype=torch.uint8, device=device)

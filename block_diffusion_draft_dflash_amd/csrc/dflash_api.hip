@@ -1,0 +1,226 @@
+// C ABI of libdflash: argument validation, error reporting, launch dispatch.
+//
+// Host checks mirror the preconditions the "qwen3_dflash.cpp" page enforces
+// with VT_CHECK (num_reqs > 0, cumulative lengths spanning the rows, matching
+// sizes), turned into status codes plus a per-thread message instead of
+// exceptions. Nothing here allocates device memory or synchronises.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "dflash_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+dflash_status fail(dflash_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+dflash_status ok() {
+  g_last_error.clear();
+  return DFLASH_OK;
+}
+
+dflash_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(DFLASH_ERR_HIP, "%s: HIP error %d (%s)", what, (int)e, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The work split is planned for the MI355X's compute-unit count so that the
+// plan (and therefore the workspace size and the bitwise result for a given
+// input) is a pure function of the parameters.
+constexpr int kPlanComputeUnits = 256;
+
+dflash_status check_head_geometry(int32_t hq, int32_t hkv, int32_t dh, bool need_q) {
+  if (hkv < 1) return fail(DFLASH_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", hkv);
+  if (need_q && hq < 1) return fail(DFLASH_ERR_INVALID_ARG, "num_q_heads must be >= 1 (got %d)", hq);
+  if (need_q && hq % hkv != 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "num_q_heads (%d) must be a multiple of num_kv_heads (%d)",
+                hq, hkv);
+  if (dh <= 0 || dh % 2 != 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "head_dim must be positive and even (got %d)", dh);
+  if (dh != 64 && dh != 128)
+    return fail(DFLASH_ERR_UNSUPPORTED, "head_dim %d is not supported (64 or 128)", dh);
+  return DFLASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_last_error(void) { return g_last_error.c_str(); }
+
+int dflash_abi_version(void) { return 100; }
+
+dflash_status dflash_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
+                                void* stream) {
+  if (!table) return fail(DFLASH_ERR_INVALID_ARG, "rope_table: table is NULL");
+  if (!aligned(table, 16)) return fail(DFLASH_ERR_INVALID_ARG, "rope_table: table not 16-byte aligned");
+  if (max_pos < 1) return fail(DFLASH_ERR_INVALID_ARG, "rope_table: max_pos must be >= 1");
+  if (head_dim < 2 || head_dim > 256 || head_dim % 2)
+    return fail(DFLASH_ERR_INVALID_ARG, "rope_table: head_dim must be even in [2, 256]");
+  if (!(theta > 0.0) || !std::isfinite(theta))
+    return fail(DFLASH_ERR_INVALID_ARG, "rope_table: theta must be positive and finite");
+  return hip_status(dflash::launch_rope_table(table, max_pos, head_dim, theta, (hipStream_t)stream),
+                    "rope_table launch");
+}
+
+dflash_status dflash_qk_norm_rope(dflash_dtype dtype, void* q, void* k, const float* q_norm_w,
+                                  const float* k_norm_w, const int32_t* positions, int64_t T,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  float eps, const float* rope_table, int32_t max_pos,
+                                  void* stream) {
+  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16)
+    return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: unknown dtype %d", (int)dtype);
+  dflash_status st = check_head_geometry(num_q_heads, num_kv_heads, head_dim, q != nullptr);
+  if (st != DFLASH_OK) return st;
+  if (T < 0) return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: T must be >= 0");
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: eps must be finite and >= 0");
+  if (max_pos < 1) return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: max_pos must be >= 1");
+  if (T == 0) return ok();
+  if (!k || !k_norm_w || !positions || !rope_table || (q && !q_norm_w))
+    return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: NULL pointer argument");
+  if (!aligned(k, 16) || (q && !aligned(q, 16)) || !aligned(k_norm_w, 16) ||
+      (q && !aligned(q_norm_w, 16)) || !aligned(rope_table, 16))
+    return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: tensors must be 16-byte aligned");
+  if (T > (int64_t)1 << 40) return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: T too large");
+  return hip_status(dflash::launch_qk_norm_rope(dtype, q, k, q_norm_w, k_norm_w, positions, T,
+                                                num_q_heads, num_kv_heads, head_dim, eps,
+                                                rope_table, max_pos, (hipStream_t)stream),
+                    "qk_norm_rope launch");
+}
+
+dflash_status dflash_block_attention_check(const dflash_block_attn_params* p) {
+  if (!p) return fail(DFLASH_ERR_INVALID_ARG, "block_attention: params is NULL");
+  if (p->dtype != DFLASH_F32 && p->dtype != DFLASH_BF16)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: unknown dtype %d", (int)p->dtype);
+  if (p->num_reqs < 1)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: num_reqs must be > 0 (got %d)", p->num_reqs);
+  dflash_status st = check_head_geometry(p->num_q_heads, p->num_kv_heads, p->head_dim, true);
+  if (st != DFLASH_OK) return st;
+  if (p->total_ctx < 0 || p->total_blk < 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: total_ctx/total_blk must be >= 0");
+  if (p->total_ctx + p->total_blk > INT32_MAX / 2)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: total rows must be < 2^30");
+  if (p->max_blk_len < 0 || p->max_blk_len > p->total_blk)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: max_blk_len must be in [0, total_blk]");
+  if (p->total_blk > 0 && p->max_blk_len < 1)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: max_blk_len must be >= 1 when total_blk > 0");
+  if ((int64_t)p->max_blk_len * (p->num_q_heads / p->num_kv_heads) > INT32_MAX / 2)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: block too long");
+  if (!std::isfinite(p->scale))
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: scale must be finite");
+  if (p->window < 0) return fail(DFLASH_ERR_INVALID_ARG, "block_attention: window must be >= 0");
+  if (p->window > 0 && !p->causal)
+    return fail(DFLASH_ERR_INVALID_ARG,
+                "block_attention: a sliding window requires causal attention");
+  if (p->split_keys < 0 || p->split_keys % 64 != 0 || p->split_keys > (1 << 24))
+    return fail(DFLASH_ERR_INVALID_ARG,
+                "block_attention: split_keys must be 0 or a positive multiple of 64 up to 2^24");
+  return ok();
+}
+
+size_t dflash_block_attention_workspace_size(const dflash_block_attn_params* p) {
+  if (dflash_block_attention_check(p) != DFLASH_OK) return 0;
+  dflash::AttnPlan plan;
+  dflash::plan_block_attention(*p, kPlanComputeUnits, &plan);
+  return plan.bytes;
+}
+
+dflash_status dflash_block_attention(const dflash_block_attn_params* p, const int32_t* cu_ctx_lens,
+                                     const int32_t* cu_blk_lens, const void* q, const void* k_blk,
+                                     const void* v_blk, const void* k_ctx, const void* v_ctx,
+                                     void* out, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+  dflash_status st = dflash_block_attention_check(p);
+  if (st != DFLASH_OK) return st;
+  if (p->total_blk == 0) return ok();
+  if (!cu_ctx_lens || !cu_blk_lens)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: cu_ctx_lens/cu_blk_lens are NULL");
+  if (!q || !k_blk || !v_blk || !out)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: q/k_blk/v_blk/out must not be NULL");
+  if (p->total_ctx > 0 && (!k_ctx || !v_ctx))
+    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: k_ctx/v_ctx are NULL but total_ctx > 0");
+  const void* tens[] = {q, k_blk, v_blk, out, k_ctx, v_ctx};
+  for (const void* t : tens)
+    if (t && !aligned(t, 16))
+      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: tensors must be 16-byte aligned");
+  dflash::AttnPlan plan;
+  dflash::plan_block_attention(*p, kPlanComputeUnits, &plan);
+  if (plan.bytes > 0) {
+    if (!workspace)
+      return fail(DFLASH_ERR_WORKSPACE, "block_attention: workspace is NULL (%zu bytes needed)",
+                  plan.bytes);
+    if (!aligned(workspace, 256))
+      return fail(DFLASH_ERR_WORKSPACE, "block_attention: workspace must be 256-byte aligned");
+    if (workspace_bytes < plan.bytes)
+      return fail(DFLASH_ERR_WORKSPACE, "block_attention: workspace has %zu bytes, %zu needed",
+                  workspace_bytes, plan.bytes);
+  }
+  if (plan.units * p->num_kv_heads > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "block_attention: too many work units");
+  return hip_status(dflash::launch_block_attention(*p, plan, cu_ctx_lens, cu_blk_lens, q, k_blk,
+                                                   v_blk, k_ctx, v_ctx, out, workspace,
+                                                   (hipStream_t)stream),
+                    "block_attention launch");
+}
+
+size_t dflash_context_kv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_kv_heads,
+                                        int32_t head_dim) {
+  if (T < 0 || hidden_size < 1 || num_kv_heads < 1 || head_dim < 1) return 0;
+  return dflash::context_kv_workspace_bytes(T, hidden_size, num_kv_heads, head_dim);
+}
+
+dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, const void* w_k,
+                                const void* w_v, const float* k_norm_w, const int32_t* positions,
+                                int64_t T, int32_t hidden_size, int32_t num_kv_heads,
+                                int32_t head_dim, float eps, const float* rope_table,
+                                int32_t max_pos, void* k_out, void* v_out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (T < 0) return fail(DFLASH_ERR_INVALID_ARG, "context_kv: T must be >= 0");
+  if (num_kv_heads < 1) return fail(DFLASH_ERR_INVALID_ARG, "context_kv: num_kv_heads must be >= 1");
+  if (head_dim != 128)
+    return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: head_dim %d is not supported (128)", head_dim);
+  if (hidden_size < 64 || hidden_size % 64 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: hidden_size must be a positive multiple of 64");
+  if ((num_kv_heads * head_dim) % 256 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: num_kv_heads * head_dim must be a multiple of 256");
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(DFLASH_ERR_INVALID_ARG, "context_kv: eps must be finite and >= 0");
+  if (max_pos < 1) return fail(DFLASH_ERR_INVALID_ARG, "context_kv: max_pos must be >= 1");
+  if (T == 0) return ok();
+  const void* ptrs[] = {hidden, hidden_norm_w, w_k, w_v, k_norm_w, positions, rope_table, k_out, v_out};
+  for (const void* t : ptrs)
+    if (!t) return fail(DFLASH_ERR_INVALID_ARG, "context_kv: NULL pointer argument");
+  const void* al[] = {hidden, hidden_norm_w, w_k, w_v, k_norm_w, rope_table, k_out, v_out};
+  for (const void* t : al)
+    if (!aligned(t, 16)) return fail(DFLASH_ERR_INVALID_ARG, "context_kv: tensors must be 16-byte aligned");
+  const size_t need = dflash::context_kv_workspace_bytes(T, hidden_size, num_kv_heads, head_dim);
+  if (need > 0) {
+    if (!workspace) return fail(DFLASH_ERR_WORKSPACE, "context_kv: workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(workspace, 256))
+      return fail(DFLASH_ERR_WORKSPACE, "context_kv: workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(DFLASH_ERR_WORKSPACE, "context_kv: workspace has %zu bytes, %zu needed",
+                  workspace_bytes, need);
+  }
+  return hip_status(dflash::launch_context_kv(hidden, hidden_norm_w, w_k, w_v, k_norm_w, positions,
+                                              T, hidden_size, num_kv_heads, head_dim, eps,
+                                              rope_table, max_pos, k_out, v_out, workspace,
+                                              (hipStream_t)stream),
+                    "context_kv launch");
+}
+
+}  // extern "C"

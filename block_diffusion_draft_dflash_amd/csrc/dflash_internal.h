@@ -1,0 +1,41 @@
+// Host-side interface between the C-ABI layer and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "dflash.h"
+
+namespace dflash {
+
+hipError_t launch_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
+                             hipStream_t s);
+
+hipError_t launch_qk_norm_rope(dflash_dtype dt, void* q, void* k, const float* wq,
+                               const float* wk, const int32_t* pos, int64_t rows, int32_t hq,
+                               int32_t hkv, int32_t dh, float eps, const float* table,
+                               int32_t max_pos, hipStream_t s);
+
+// Work decomposition of one block-attention call (host side, no device access).
+struct AttnPlan {
+  int32_t group;      // Hq / Hkv
+  int32_t qtiles;     // bound on 64-row query tiles per (request, kv-head)
+  int32_t chunk;      // keys per work unit (multiple of 64)
+  int64_t units;      // bound on work units per kv-head (grid = units * Hkv)
+  size_t off_counters, off_part_o, off_part_ml, bytes;
+};
+bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPlan* plan);
+
+hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnPlan& plan,
+                                  const int32_t* cu_ctx, const int32_t* cu_blk, const void* q,
+                                  const void* kb, const void* vb, const void* kc, const void* vc,
+                                  void* out, void* ws, hipStream_t s);
+
+size_t context_kv_workspace_bytes(int64_t rows, int32_t hidden, int32_t hkv, int32_t dh);
+hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* wk,
+                             const void* wv, const float* knw, const int32_t* pos, int64_t rows,
+                             int32_t hidden_size, int32_t hkv, int32_t dh, float eps,
+                             const float* table, int32_t max_pos, void* k_out, void* v_out,
+                             void* ws, hipStream_t s);
+
+}  // namespace dflash

@@ -1,0 +1,121 @@
+"""Device-side driver of one synthetic batch through libdflash.
+
+Uploads a :class:`~block_diffusion_draft_dflash_amd.workloads.Workload` to the
+GPU, builds the RoPE cos/sin cache and the workspaces, and runs the path
+through the C ABI:
+
+* context rows: ``dflash_context_kv`` from hidden states when the workload has
+  them, else the K-only ``dflash_qk_norm_rope`` on the raw context keys;
+* the step: ``dflash_qk_norm_rope`` on the block's q and k (in place), then
+  ``dflash_block_attention`` over [context; block].
+
+Only argument marshalling happens here; every step runs in the HIP library.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+import torch
+
+from . import binding as B
+from .workloads import Workload, f32_to_bf16_bits
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    """Upload float32 values (bf16-representable for bf16) without rounding changes."""
+    if dtype == "bf16":
+        bits = f32_to_bf16_bits(x)
+        return torch.from_numpy(bits.view(np.int16)).to(device).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(device)
+
+
+def bits_to_device(bits: np.ndarray, device="cuda") -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(device).view(torch.bfloat16)
+
+
+def to_host_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class DevicePath:
+    def __init__(self, wl: Workload, device: str = "cuda", split_keys: int = 0,
+                 max_pos: Optional[int] = None):
+        self.wl = wl
+        self.device = device
+        dt = wl.dtype
+        self.dtype_code = B.DFLASH_BF16 if dt == "bf16" else B.DFLASH_F32
+        i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(device)
+        self.cu_ctx = i32(wl.cu_ctx)
+        self.cu_blk = i32(wl.cu_blk)
+        self.ctx_pos = i32(wl.ctx_positions)
+        self.blk_pos = i32(wl.blk_positions)
+        self.q = to_device(wl.q, dt, device)
+        self.k_blk = to_device(wl.k_blk, dt, device)
+        self.v_blk = to_device(wl.v_blk, dt, device)
+        f32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(device)
+        self.q_norm_w = f32(wl.q_norm_w)
+        self.k_norm_w = f32(wl.k_norm_w)
+        if max_pos is None:
+            mp = 1
+            if wl.ctx_positions.size:
+                mp = max(mp, int(wl.ctx_positions.max()) + 1)
+            if wl.blk_positions.size:
+                mp = max(mp, int(wl.blk_positions.max()) + 1)
+            max_pos = mp
+        self.max_pos = max_pos
+        self.rope = torch.empty((max_pos, wl.dh // 2, 2), dtype=torch.float32, device=device)
+        B.dflash_rope_table(self.rope, max_pos, wl.dh, wl.theta)
+        tc = wl.total_ctx
+        if wl.hidden is not None:
+            self.hidden = bits_to_device(wl.hidden, device)
+            self.hidden_norm_w = f32(wl.hidden_norm_w)
+            self.w_k = bits_to_device(wl.w_k, device)
+            self.w_v = bits_to_device(wl.w_v, device)
+            tdt = torch.bfloat16
+            self.k_ctx = torch.empty((tc, wl.hkv, wl.dh), dtype=tdt, device=device)
+            self.v_ctx = torch.empty((tc, wl.hkv, wl.dh), dtype=tdt, device=device)
+            ckv_ws = B.dflash_context_kv_workspace_size(tc, wl.hidden_size, wl.hkv, wl.dh)
+            self.ckv_ws = B.alloc_workspace(ckv_ws, device)
+            self.k_ctx_raw = None
+        else:
+            self.hidden = None
+            self.k_ctx_raw = to_device(wl.k_ctx, dt, device)
+            self.k_ctx = self.k_ctx_raw.clone()
+            self.v_ctx = to_device(wl.v_ctx, dt, device)
+        self.out = torch.zeros_like(self.q)
+        self.params = B.make_block_attn_params(
+            wl.num_reqs, wl.hq, wl.hkv, wl.dh, self.dtype_code, tc, wl.total_blk,
+            int(wl.blk_lens.max()) if wl.num_reqs else 0, wl.scale, wl.causal, wl.window,
+            split_keys)
+        self.ws = B.alloc_workspace(B.dflash_block_attention_workspace_size(self.params), device)
+
+    # ---------------------------------------------------------------- context
+    def prepare_context(self) -> None:
+        """Produce the normed + rotated context keys (and V for hidden-state input)."""
+        wl = self.wl
+        if self.hidden is not None:
+            B.dflash_context_kv(self.hidden, self.hidden_norm_w, self.w_k, self.w_v,
+                                self.k_norm_w, self.ctx_pos, wl.hkv, wl.dh, wl.eps, self.rope,
+                                self.k_ctx, self.v_ctx, self.ckv_ws)
+        else:
+            self.k_ctx.copy_(self.k_ctx_raw)
+            if wl.total_ctx:
+                B.dflash_qk_norm_rope(None, self.k_ctx, None, self.k_norm_w, self.ctx_pos,
+                                      wl.eps, self.rope)
+
+    # ---------------------------------------------------------------- step
+    def qk_norm_rope(self) -> None:
+        if self.wl.total_blk:
+            B.dflash_qk_norm_rope(self.q, self.k_blk, self.q_norm_w, self.k_norm_w,
+                                  self.blk_pos, self.wl.eps, self.rope)
+
+    def attention(self) -> None:
+        B.dflash_block_attention(self.params, self.cu_ctx, self.cu_blk, self.q, self.k_blk,
+                                 self.v_blk, self.k_ctx if self.wl.total_ctx else None,
+                                 self.v_ctx if self.wl.total_ctx else None, self.out, self.ws)
+
+    def step(self) -> None:
+        """One pass of the hot path over the batch: q/k norm + RoPE, block attention."""
+        self.qk_norm_rope()
+        self.attention()

@@ -1,0 +1,197 @@
+/*
+ * dflash.h -- C ABI of libdflash: the DFlash draft model's block attention on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What is computed. On the "qwen3_dflash.cpp" page (file header,
+ * ForwardWithCtxKVDev, ForwardPagedBody) each speculative block of B query
+ * tokens of a request attends over that request's C precomputed context K/V
+ * rows followed by the block's own K/V rows. Full-attention layers see the
+ * whole [context; block] sequence (bidirectional inside the block); sliding
+ * window layers are causal with a window. Heads use grouped-query attention;
+ * q and k get a per-head RMSNorm and a NeoX rotary embedding before the
+ * attention. The context rows come from the hidden-state RMSNorm, the K/V
+ * projection, the per-head k-norm and RoPE (PrecomputeContextKVDevice).
+ *
+ * Conventions shared by every call.
+ *   - All tensor pointers are DEVICE pointers unless stated otherwise; all
+ *     tensors are dense row-major with no padding, and 16-byte aligned.
+ *   - "bf16" is bfloat16 (round to nearest even on every store); "f32" is IEEE
+ *     binary32. Arithmetic is f32 in every kernel (bf16 matrix-core products
+ *     accumulate in f32).
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *     call only enqueues work on it: no host synchronisation, no allocation,
+ *     so the calls may be captured into a HIP graph.
+ *   - The caller owns every buffer (inputs, outputs, workspaces). The library
+ *     keeps no state between calls.
+ *   - Errors: a call returns a negative dflash_status and leaves a message for
+ *     dflash_last_error() (per thread). Argument errors are detected on the
+ *     host before anything is enqueued. Integer metadata that lives on the
+ *     device (cumulative lengths, positions) is trusted to be consistent with
+ *     the host-side sizes; kernels clamp every index they derive from it to the
+ *     buffers' extents, so inconsistent metadata gives wrong results, never an
+ *     out-of-bounds access.
+ *
+ * Head geometry: Hq query heads, Hkv key/value heads (Hq % Hkv == 0), head
+ * dimension Dh in {64, 128}. q-head h reads kv-head h / (Hq / Hkv).
+ */
+#ifndef DFLASH_H_
+#define DFLASH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DFLASH_OK = 0,
+  DFLASH_ERR_INVALID_ARG = -1, /* bad size, pointer, alignment or flag */
+  DFLASH_ERR_UNSUPPORTED = -2, /* valid but not implemented (e.g. Dh = 96) */
+  DFLASH_ERR_WORKSPACE = -3,   /* workspace missing, misaligned or too small */
+  DFLASH_ERR_HIP = -4          /* the HIP runtime reported an error */
+} dflash_status;
+
+typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+
+/* Message of the last failed call on this thread ("" if none). Never NULL. */
+const char* dflash_last_error(void);
+
+/* ABI version of this header (major * 100 + minor). */
+int dflash_abi_version(void);
+
+/*
+ * dflash_rope_table -- the NeoX rotary cos/sin cache.
+ *
+ * Fills table[p][i] = {cos(p * f_i), sin(p * f_i)} for p in [0, max_pos) and
+ * i in [0, head_dim / 2), with f_i = theta^(-2 i / head_dim); angles, cos and
+ * sin are evaluated in f64 and rounded once to f32. This is the cos|sin cache
+ * the "qwen3.cpp" page (file header) keeps for RoPE; the rotation itself is
+ * RopeNeox on the "qwen3_dflash.cpp" page.
+ *
+ *   table    device f32, max_pos * head_dim elements (pairs), written.
+ *   max_pos  >= 1; head_dim even, 2..256; theta > 0.
+ */
+dflash_status dflash_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
+                                void* stream);
+
+/*
+ * dflash_qk_norm_rope -- per-head RMSNorm of q and k, then NeoX RoPE, in place.
+ *
+ * For every row t and head h of q [T, Hq, Dh] and k [T, Hkv, Dh]:
+ *   y = x * w / sqrt(mean(x^2) + eps)           (w = q_norm_w or k_norm_w)
+ *   (y_i, y_{i+Dh/2}) <- (y_i c - y_{i+Dh/2} s, y_{i+Dh/2} c + y_i s)
+ * with (c, s) = rope_table[positions[t]][i]. "qwen3_dflash.cpp" page,
+ * ForwardBlockLogits: q_norm and k_norm (standard RMSNorm over head_dim), then
+ * RopeNeox at the block positions; "qwen3.cpp" page header: norm before RoPE.
+ *
+ *   dtype      DFLASH_BF16 or DFLASH_F32, for q and k.
+ *   q          [T, Hq, Dh] in/out, or NULL for the K-only form (context rows).
+ *   k          [T, Hkv, Dh] in/out (not NULL).
+ *   q_norm_w   f32 [Dh] (ignored when q is NULL), k_norm_w f32 [Dh].
+ *   positions  int32 [T]; a position outside [0, max_pos) is clamped into it.
+ *   rope_table f32 [max_pos][Dh/2][2] from dflash_rope_table.
+ *   T may be 0 (nothing is enqueued).
+ */
+dflash_status dflash_qk_norm_rope(dflash_dtype dtype, void* q, void* k, const float* q_norm_w,
+                                  const float* k_norm_w, const int32_t* positions, int64_t T,
+                                  int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                                  float eps, const float* rope_table, int32_t max_pos,
+                                  void* stream);
+
+/*
+ * Block attention parameters (host values). Mirrors the arguments of the
+ * block attention call on the "qwen3_dflash.cpp" page ({scale, causal,
+ * sliding_window, cu_seqlens, num_reqs}) with the context and block rows given
+ * as two separate packed sources instead of one materialised sequence.
+ */
+typedef struct {
+  int32_t num_reqs;     /* R >= 1 */
+  int32_t num_q_heads;  /* Hq */
+  int32_t num_kv_heads; /* Hkv, divides Hq */
+  int32_t head_dim;     /* Dh in {64, 128} */
+  dflash_dtype dtype;   /* of q, k_*, v_*, out */
+  int64_t total_ctx;    /* rows of k_ctx / v_ctx (= cu_ctx_lens[R]) */
+  int64_t total_blk;    /* rows of q / k_blk / v_blk / out (= cu_blk_lens[R]) */
+  int32_t max_blk_len;  /* upper bound on any request's block length */
+  float scale;          /* softmax scale, 1/sqrt(Dh) on the pages */
+  int32_t causal;       /* 0: bidirectional, else causal */
+  int32_t window;       /* 0: none; > 0 (causal only): keys with i - k < window */
+  int32_t split_keys;   /* keys per work unit; 0 = chosen by the library,
+                           else a positive multiple of 64 */
+} dflash_block_attn_params;
+
+/* Bytes of workspace dflash_block_attention needs for these parameters
+ * (0 if they are invalid; see dflash_block_attention_check). */
+size_t dflash_block_attention_workspace_size(const dflash_block_attn_params* p);
+
+/* Host-side validation only: the status dflash_block_attention would return
+ * for these parameters before touching any pointer. */
+dflash_status dflash_block_attention_check(const dflash_block_attn_params* p);
+
+/*
+ * dflash_block_attention -- softmax(scale Q K^T) V of each block over its
+ * request's [context; block] keys.
+ *
+ * Request r owns context rows [cu_ctx_lens[r], cu_ctx_lens[r+1]) of k_ctx/v_ctx
+ * and block rows [cu_blk_lens[r], cu_blk_lens[r+1]) of q/k_blk/v_blk/out. In
+ * its combined sequence the context rows take indices 0..C-1 and the block rows
+ * C..C+B-1; block query b sits at index C+b. Key k is visible to it always
+ * (causal == 0), or iff k <= C+b and (window == 0 or C+b-k < window). Only block
+ * queries are computed ("qwen3_dflash.cpp" page, ForwardWithCtxKVDev keeps only
+ * the block rows of the combined attention; ForwardPagedBody computes them
+ * directly).
+ *
+ *   cu_ctx_lens, cu_blk_lens  device int32 [R+1], nondecreasing, [0] = 0.
+ *   q       [total_blk, Hq, Dh]  (already q-normed and rotated)
+ *   k_blk   [total_blk, Hkv, Dh] (already k-normed and rotated), v_blk alike.
+ *   k_ctx   [total_ctx, Hkv, Dh], v_ctx alike; may be NULL if total_ctx == 0.
+ *   out     [total_blk, Hq, Dh], written (rows of empty requests untouched).
+ *   workspace  device, 256-byte aligned, >= dflash_block_attention_workspace_size
+ *           bytes, ZERO-FILLED before its first use; every call leaves it
+ *           zero-filled again where it must be. One workspace must not be used
+ *           by two calls that may run concurrently.
+ * The result does not depend on how the keys are split into work units other
+ * than through f32 rounding; for a fixed split_keys it is bitwise
+ * deterministic.
+ */
+dflash_status dflash_block_attention(const dflash_block_attn_params* p, const int32_t* cu_ctx_lens,
+                                     const int32_t* cu_blk_lens, const void* q, const void* k_blk,
+                                     const void* v_blk, const void* k_ctx, const void* v_ctx,
+                                     void* out, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+/*
+ * dflash_context_kv -- context K/V precompute (bf16).
+ *
+ * For each context row t: n = RMSNorm(hidden[t], hidden_norm_w); K = n W_k^T,
+ * V = n W_v^T; K <- per-head RMSNorm(K, k_norm_w); K <- NeoX RoPE at
+ * positions[t]; V stays raw. "qwen3_dflash.cpp" page,
+ * PrecomputeContextKVDevice (W_k and W_v are the K and V row slices of the
+ * merged qkv weight; the result is the ContextKVDev record).
+ *
+ *   hidden        bf16 [T, H]
+ *   hidden_norm_w f32 [H];  w_k, w_v bf16 [Hkv*Dh, H];  k_norm_w f32 [Dh]
+ *   positions     int32 [T], clamped into [0, max_pos)
+ *   rope_table    f32 [max_pos][Dh/2][2] from dflash_rope_table
+ *   k_out, v_out  bf16 [T, Hkv, Dh], written
+ *   workspace     device, 256-byte aligned, >= dflash_context_kv_workspace_size
+ *                 bytes (no zero-fill needed)
+ * Requirements: Dh == 128, H % 64 == 0, (Hkv * Dh) % 256 == 0. Each output row
+ * depends only on its own input row, so splitting the rows across calls gives
+ * bitwise identical results.
+ */
+size_t dflash_context_kv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_kv_heads,
+                                        int32_t head_dim);
+dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, const void* w_k,
+                                const void* w_v, const float* k_norm_w, const int32_t* positions,
+                                int64_t T, int32_t hidden_size, int32_t num_kv_heads,
+                                int32_t head_dim, float eps, const float* rope_table,
+                                int32_t max_pos, void* k_out, void* v_out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DFLASH_H_ */

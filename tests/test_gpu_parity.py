@@ -1,0 +1,183 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Bars (written here, from the method's stated tolerances):
+  * bf16 attention output: max |gpu - oracle| <= 2e-2 and mean |gpu - oracle| <= 2e-3
+    over all compared elements;
+  * f32 attention output: max |gpu - oracle| / max |oracle| <= 1e-4;
+  * intermediates (normed + rotated q/k, context K/V) are compared against the
+    rounding they carry: one bf16 rounding of an f32 result (relative 2^-9)
+    plus f32 arithmetic, i.e. |gpu - oracle| <= 2^-7 |oracle| + 1e-5 for
+    q/k, and for the projected context K/V a scale-relative bound of 1e-2
+    (bf16 weight folding and bf16 storage).
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_dflash_amd.pipeline import DevicePath, to_host_f64
+from block_diffusion_draft_dflash_amd.workloads import bf16_bits_to_f32, make_workload
+from oracle import dflash_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+BF16_MAX_ABS = 2e-2
+BF16_MEAN_ABS = 2e-3
+F32_REL = 1e-4
+
+
+def sub_batch_inputs(wl, reqs):
+    """The oracle's inputs restricted to the listed requests (re-based lengths)."""
+    q, kb, vb, bpos, kc, vc, cpos, cu_c, cu_b, hid = [], [], [], [], [], [], [], [0], [0], []
+    for r in reqs:
+        c0, c1 = int(wl.cu_ctx[r]), int(wl.cu_ctx[r + 1])
+        b0, b1 = int(wl.cu_blk[r]), int(wl.cu_blk[r + 1])
+        q.append(wl.q[b0:b1]); kb.append(wl.k_blk[b0:b1]); vb.append(wl.v_blk[b0:b1])
+        bpos.append(wl.blk_positions[b0:b1]); cpos.append(wl.ctx_positions[c0:c1])
+        if wl.hidden is not None:
+            hid.append(bf16_bits_to_f32(wl.hidden[c0:c1]))
+        else:
+            kc.append(wl.k_ctx[c0:c1]); vc.append(wl.v_ctx[c0:c1])
+        cu_c.append(cu_c[-1] + c1 - c0); cu_b.append(cu_b[-1] + b1 - b0)
+    cat = lambda xs: np.concatenate(xs) if xs else None
+    return dict(q=cat(q), k_blk=cat(kb), v_blk=cat(vb), blk_pos=cat(bpos), ctx_pos=cat(cpos),
+                k_ctx=cat(kc), v_ctx=cat(vc), hidden=cat(hid), cu_ctx=np.array(cu_c),
+                cu_blk=np.array(cu_b))
+
+
+def oracle_outputs(wl, reqs=None):
+    reqs = list(range(wl.num_reqs)) if reqs is None else reqs
+    s = sub_batch_inputs(wl, reqs)
+    if wl.hidden is not None:
+        k_ctx, v_ctx = O.context_kv(s["hidden"], wl.hidden_norm_w, bf16_bits_to_f32(wl.w_k),
+                                    bf16_bits_to_f32(wl.w_v), wl.k_norm_w, s["ctx_pos"], wl.hkv,
+                                    wl.dh, wl.eps, wl.theta)
+    else:
+        _, k_ctx = O.qk_norm_rope(None, s["k_ctx"], None, wl.k_norm_w, s["ctx_pos"], wl.eps,
+                                  wl.theta)
+        v_ctx = s["v_ctx"]
+    out, q_hat, k_hat = O.draft_block_attention(
+        s["q"], s["k_blk"], s["v_blk"], s["blk_pos"], k_ctx, v_ctx, s["cu_ctx"], s["cu_blk"],
+        wl.q_norm_w, wl.k_norm_w, wl.eps, wl.theta, wl.scale, wl.causal, wl.window)
+    return dict(out=out, q_hat=q_hat, k_hat=k_hat, k_ctx=k_ctx, v_ctx=v_ctx)
+
+
+def gpu_rows(wl, t, reqs, ctx=False):
+    cu = wl.cu_ctx if ctx else wl.cu_blk
+    idx = np.concatenate([np.arange(cu[r], cu[r + 1]) for r in reqs]) if reqs else np.zeros(0, int)
+    return to_host_f64(t)[idx]
+
+
+def assert_output(wl, got, ref, tag=""):
+    err = np.abs(got - ref)
+    if wl.dtype == "f32":
+        rel = err.max() / max(np.abs(ref).max(), 1e-30)
+        print(f"[{tag}] f32 rel err {rel:.3e}")
+        assert rel <= F32_REL, f"{tag}: relative error {rel:.3e} > {F32_REL}"
+    else:
+        print(f"[{tag}] max abs {err.max():.3e} mean abs {err.mean():.3e} (|ref| max {np.abs(ref).max():.3f})")
+        assert err.max() <= BF16_MAX_ABS, f"{tag}: max abs err {err.max():.3e}"
+        assert err.mean() <= BF16_MEAN_ABS, f"{tag}: mean abs err {err.mean():.3e}"
+
+
+def assert_rounded(wl, got, ref, tag):
+    rel = 2.0 ** -7 if wl.dtype == "bf16" else 1e-6
+    bad = np.abs(got - ref) > rel * np.abs(ref) + 1e-5
+    print(f"[{tag}] max abs {np.abs(got - ref).max():.3e}")
+    assert not bad.any(), f"{tag}: {bad.sum()} elements beyond one-rounding bound"
+
+
+def run_and_check(wl, split_keys=0, reqs=None, check_intermediates=True, tag=""):
+    torch.cuda.synchronize()
+    dp = DevicePath(wl, split_keys=split_keys)
+    dp.prepare_context()
+    dp.step()
+    torch.cuda.synchronize()
+    reqs = list(range(wl.num_reqs)) if reqs is None else reqs
+    ref = oracle_outputs(wl, reqs)
+    assert_output(wl, gpu_rows(wl, dp.out, reqs), ref["out"], tag)
+    if check_intermediates:
+        assert_rounded(wl, gpu_rows(wl, dp.q, reqs), ref["q_hat"], tag + " q_hat")
+        assert_rounded(wl, gpu_rows(wl, dp.k_blk, reqs), ref["k_hat"], tag + " k_blk_hat")
+        gk = gpu_rows(wl, dp.k_ctx, reqs, ctx=True)
+        if wl.hidden is None:
+            assert_rounded(wl, gk, ref["k_ctx"], tag + " k_ctx_hat")
+        else:
+            gv = gpu_rows(wl, dp.v_ctx, reqs, ctx=True)
+            for name, g, o in (("k_ctx", gk, ref["k_ctx"]), ("v_ctx", gv, ref["v_ctx"])):
+                rel = np.abs(g - o).max() / np.abs(o).max()
+                print(f"[{tag} {name}] scale-relative max err {rel:.3e}")
+                assert rel <= 1e-2, f"{tag} {name}: {rel:.3e}"
+    return dp
+
+
+# ---------------------------------------------------------------- small sizes (full oracle)
+
+SMALL = {
+    "tiny": dict(),
+    "qwen3_8b_draft": dict(num_reqs=3, ctx_lo=100, ctx_hi=700),
+    "large_decode": dict(num_reqs=70, ctx_lo=1, ctx_hi=300),
+    "swa": dict(num_reqs=3, ctx_len=700, window=256),
+    "ctx_kv": dict(num_reqs=2, ctx_len=300, hidden=512),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_parity_small(name):
+    print(f"case small {name}", flush=True)
+    wl = make_workload(name, **SMALL[name])
+    run_and_check(wl, tag=f"small {name}")
+
+
+@pytest.mark.parametrize("split", [64, 128, 4096])
+def test_parity_forced_splits(split):
+    print(f"case split {split}", flush=True)
+    wl = make_workload("qwen3_8b_draft", num_reqs=3, ctx_lo=100, ctx_hi=700)
+    run_and_check(wl, split_keys=split, check_intermediates=False, tag=f"split {split}")
+
+
+EDGE = {
+    "empty_ctx_and_blocks": dict(name="qwen3_8b_draft", ctx_lens=[0, 5, 130, 0, 77],
+                                 blk_lens=[3, 0, 17, 40, 1]),
+    "gqa1": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=200, hq=8, hkv=8),
+    "gqa8": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=200, hq=64, hkv=8),
+    "dh64_bf16": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=50, ctx_hi=300, hq=8, hkv=2, dh=64),
+    "causal_nowindow": dict(name="swa", num_reqs=3, ctx_len=200, window=0),
+    "window1": dict(name="swa", num_reqs=2, ctx_len=100, window=1),
+    "window_gt_len": dict(name="swa", num_reqs=2, ctx_len=100, window=5000),
+    "causal_long_block": dict(name="swa", ctx_lens=[40, 0], blk_lens=[70, 33], window=50),
+    "f32_varlen": dict(name="tiny", ctx_lens=[0, 64, 129], blk_lens=[16, 5, 0], hq=8, hkv=2, dh=128),
+    "f32_causal": dict(name="tiny", ctx_lens=[64, 10], blk_lens=[16, 16], causal=True, window=20),
+}
+
+
+@pytest.mark.parametrize("case", list(EDGE))
+def test_parity_edges(case):
+    print(f"case edge {case}", flush=True)
+    kw = dict(EDGE[case])
+    name = kw.pop("name")
+    wl = make_workload(name, **kw)
+    run_and_check(wl, tag=f"edge {case}")
+
+
+# ---------------------------------------------------------------- full sizes (sampled)
+
+def test_parity_full_qwen3_8b_draft():
+    print("case full qwen3_8b_draft", flush=True)
+    wl = make_workload("qwen3_8b_draft")
+    run_and_check(wl, tag="full qwen3_8b_draft")
+
+
+def test_parity_full_large_decode_sampled():
+    print("case full large_decode", flush=True)
+    wl = make_workload("large_decode")
+    order = np.argsort(wl.ctx_lens)
+    reqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2]), 1, 17, 63})
+    run_and_check(wl, reqs=reqs, tag="full large_decode sampled")
+
+
+def test_parity_full_swa_sampled():
+    print("case full swa", flush=True)
+    wl = make_workload("swa")
+    run_and_check(wl, reqs=[0, 7, 15], tag="full swa sampled")
