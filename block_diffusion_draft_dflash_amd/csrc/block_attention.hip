@@ -24,6 +24,8 @@
 //   (unnormalised O, running max, sum); the last unit to finish (integer
 //   ticket per (request, query tile, kv-head)) merges them in split order, so
 //   the result is deterministic.
+#include <mutex>
+
 #include "dflash_device.h"
 #include "dflash_internal.h"
 
@@ -31,7 +33,7 @@ namespace dflash {
 namespace {
 
 constexpr int QROWS = 64;  // query rows per work unit
-constexpr int KT = 64;     // keys per tile
+constexpr int KT = 32;     // keys per tile
 constexpr int NT = 256;    // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 
@@ -46,7 +48,7 @@ struct AttnArgs {
   bf16* out;
   float* part_o;      // [units * hkv][QROWS][DH]
   float* part_ml;     // [units * hkv][QROWS][2]
-  int32_t* counters;  // [R][qtiles][hkv]
+  int32_t* dir;       // [R][qtiles][hkv]: first unit index of each split set
   int64_t total_ctx, total_blk;
   int32_t num_reqs, hq, hkv, group, chunk, qtiles, max_blk;
   float scale_log2;
@@ -134,29 +136,68 @@ __device__ bool find_unit(const AttnArgs& a, int32_t u, Unit* out) {
   return false;
 }
 
-// Physical 16-byte chunk of logical chunk c in LDS row `row` (bank spreading).
+// Physical 16-byte chunk of logical chunk c in LDS row `row`: XOR with a
+// row-dependent mask (its own inverse). K rows are read 16 rows x one chunk at
+// a time (b128), so the 16 rows of a sub-tile must hit distinct 16-byte bank
+// groups. V rows are read by the transpose loads 4 rows x 32 bytes per 16
+// lanes; the V mask keeps chunk pairs adjacent and gives the 8 rows read
+// by 32 lanes distinct 32-byte bank windows.
 template <int DH>
-__device__ __forceinline__ int swz(int row, int c) {
+__device__ __forceinline__ int swz_k(int row, int c) {
   if constexpr (DH == 128) return c ^ (row & 15);
   else return c ^ ((row >> 1) & 7);
 }
+template <int DH>
+__device__ __forceinline__ int swz_v(int row, int c) {
+  if constexpr (DH == 128) return c ^ ((row & 7) << 1);
+  else return c ^ (((row >> 1) & 3) << 1);
+}
+
+__device__ __forceinline__ int32_t uni(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+// Workgroup barrier without the memory fence __syncthreads() carries (that
+// fence would drain every outstanding load, including prefetched tiles).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+constexpr int NSTAGE = 4;  // LDS stages: NSTAGE - 1 tiles in flight
 
 template <int DH>
 __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
-  constexpr int CH = DH / 8;             // 16-byte chunks per row
-  constexpr int DS = DH / 32;            // MFMA k-steps over the head dim
-  constexpr int DT = DH / 16;            // 16-wide d tiles of O^T
-  constexpr int LOADS = KT * CH / NT;    // 16-byte loads per thread per tensor per tile
+  constexpr int CH = DH / 8;                 // 16-byte chunks per row
+  constexpr int DS = DH / 32;                // MFMA k-steps over the head dim
+  constexpr int DT = DH / 16;                // 16-wide d tiles of O^T
+  constexpr int ROWS_PER_INST = 64 / CH;     // rows one wave-wide 16-byte load fills (1 KB)
+  constexpr int LPW = KT / ROWS_PER_INST / 4;  // such loads per wave per tensor per tile
+  constexpr int LPT = 2 * LPW;               // per thread per tile (K and V)
   constexpr int TILE_ELEMS = KT * DH;
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][K|V][KT*DH]
+  constexpr int STAGE_ELEMS = 2 * TILE_ELEMS;
+  static_assert(LPW >= 1, "tile too small");
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][K | V][KT][DH]
 
   const int32_t g = blockIdx.x % a.hkv;
   const int32_t u = blockIdx.x / a.hkv;
   Unit un;
   if (!find_unit(a, u, &un)) return;  // uniform over the workgroup
+  // Every lane holds the same unit; say so to the compiler (scalar registers,
+  // scalar branches).
+  un.r = uni(un.r); un.qt = uni(un.qt); un.s = uni(un.s); un.nsplit = uni(un.nsplit);
+  un.first = uni(un.first); un.clen = uni(un.clen); un.blen = uni(un.blen); un.lo = uni(un.lo);
+  un.ctx0 = uni(un.ctx0); un.blk0 = uni(un.blk0);
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int m = lane & 15;   // query row within the wave / MFMA column
   const int j = lane >> 4;   // lane group
@@ -185,98 +226,124 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
       qf[ds] = bf16x8{};
   }
 
-  // Tile loader: thread tid moves chunks tid, tid+256, ... of the K and V tiles.
-  bf16x8 kreg[LOADS], vreg[LOADS];
-  auto load_tile = [&](int32_t kt0) {
+  // Tile loader: direct global -> LDS copies. One wave-wide load fills 1 KB of
+  // LDS (ROWS_PER_INST rows) in lane order, so each lane fetches the logical
+  // chunk that the swizzle places at its slot. A lane's row inside the tile
+  // and its chunks are fixed, so only the tile's uniform base changes. Tiles
+  // wholly inside the context (or wholly inside the block) take that path;
+  // a tile that straddles the two or runs past the range end resolves each
+  // lane's key, re-reading the last valid key for positions past the end
+  // (finite data whose scores are masked to -inf).
+  const int32_t rstride = a.hkv * DH;
+  const bf16* kc_g = a.kc + (int64_t)g * DH;
+  const bf16* vc_g = a.vc + (int64_t)g * DH;
+  const bf16* kb_g = a.kb + (int64_t)g * DH;
+  const bf16* vb_g = a.vb + (int64_t)g * DH;
+  int lrow[LPW], koff[LPW], voff[LPW];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int id = tid + NT * it;
-      const int kk = id / CH;
-      const int c = id % CH;
-      const int32_t kidx = kt0 + kk;
-      const bf16* ks = nullptr;
-      const bf16* vs = nullptr;
-      if (kidx < k_end) {
-        if (kidx < un.clen) {
-          const int64_t row = (int64_t)un.ctx0 + kidx;
-          if (row < a.total_ctx) {
-            const int64_t off = (row * a.hkv + g) * DH + c * 8;
-            ks = a.kc + off;
-            vs = a.vc + off;
-          }
-        } else {
-          const int64_t row = (int64_t)un.blk0 + (kidx - un.clen);
-          if (row < a.total_blk) {
-            const int64_t off = (row * a.hkv + g) * DH + c * 8;
-            ks = a.kb + off;
-            vs = a.vb + off;
-          }
-        }
-      }
-      kreg[it] = ks ? *reinterpret_cast<const bf16x8*>(ks) : bf16x8{};
-      vreg[it] = vs ? *reinterpret_cast<const bf16x8*>(vs) : bf16x8{};
-    }
+  for (int i = 0; i < LPW; ++i) {
+    const int q = w * LPW + i;
+    lrow[i] = q * ROWS_PER_INST + lane / CH;
+    koff[i] = lrow[i] * rstride + swz_k<DH>(lrow[i], lane % CH) * 8;
+    voff[i] = lrow[i] * rstride + swz_v<DH>(lrow[i], lane % CH) * 8;
+  }
+  auto dma = [](const bf16* src, bf16* dst) {
+    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                     (DF_LDS void*)dst, 16, 0, 0);
   };
-  auto store_tile = [&](int st) {
-    bf16* kd = smem + st * 2 * TILE_ELEMS;
-    bf16* vd = kd + TILE_ELEMS;
+  auto issue_tile = [&](int32_t t) {
+    const int32_t kt0 = k_begin + t * KT;
+    bf16* st = smem + (t % NSTAGE) * STAGE_ELEMS;
+    if (kt0 + KT <= min(un.clen, k_end)) {
+      const int64_t base = (int64_t)(un.ctx0 + kt0) * rstride;
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int id = tid + NT * it;
-      const int kk = id / CH;
-      const int c = id % CH;
-      const int off = kk * DH + swz<DH>(kk, c) * 8;
-      *reinterpret_cast<bf16x8*>(kd + off) = kreg[it];
-      *reinterpret_cast<bf16x8*>(vd + off) = vreg[it];
+      for (int i = 0; i < LPW; ++i) {
+        const int q = w * LPW + i;
+        dma(kc_g + base + koff[i], st + q * 512);
+        dma(vc_g + base + voff[i], st + TILE_ELEMS + q * 512);
+      }
+    } else if (kt0 >= un.clen && kt0 + KT <= k_end) {
+      const int64_t base = (int64_t)(un.blk0 + kt0 - un.clen) * rstride;
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int q = w * LPW + i;
+        dma(kb_g + base + koff[i], st + q * 512);
+        dma(vb_g + base + voff[i], st + TILE_ELEMS + q * 512);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LPW; ++i) {
+        const int q = w * LPW + i;
+        const int32_t kidx = min(kt0 + lrow[i], k_end - 1);
+        const bool in_ctx = kidx < un.clen;
+        const int32_t r = in_ctx ? un.ctx0 + kidx : un.blk0 + (kidx - un.clen);
+        const int64_t rbase = (int64_t)(r - lrow[i]) * rstride;
+        dma((in_ctx ? kc_g : kb_g) + rbase + koff[i], st + q * 512);
+        dma((in_ctx ? vc_g : vb_g) + rbase + voff[i], st + TILE_ELEMS + q * 512);
+      }
     }
   };
 
   f32x4 acc_o[DT];
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc_o[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float mx = -INFINITY;  // running max (log2 domain) of this lane's query row
+  float mx = -INFINITY;  // reference max (log2 domain) of this lane's query row
   float lsum = 0.f;      // this lane's share of the running sum
 
   // Masking is needed on tiles with keys past the range end, or that reach
   // beyond the first query (causal) or before the last query's window.
-  const int32_t qmin = un.clen;                 // smallest query index
-  const int32_t qmax = un.clen + un.blen - 1;   // largest query index
+  const int32_t qmin = un.clen;
+  const int32_t qmax = un.clen + un.blen - 1;
+  constexpr float TAU = 8.0f;  // rescale only when a row max grows by > 2^8
 
-  load_tile(k_begin);
-  store_tile(0);
-  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NSTAGE - 1; ++t)
+    if (t < ntiles) issue_tile(t);
+
+  const int src_row = 4 * j + (m >> 2);
+  const int src_col4 = (m & 3) * 4;
 
   for (int32_t it = 0; it < ntiles; ++it) {
-    const int st = it & 1;
-    const int32_t kt0 = k_begin + it * KT;
-    const bool has_next = it + 1 < ntiles;
-    if (has_next) load_tile(kt0 + KT);
+    // Own loads of tile `it` landed (tiles issued after it may stay in flight),
+    // then the barrier makes every wave's part visible and frees stage it-1.
+    const int32_t after = min(ntiles - 1 - it, NSTAGE - 2);
+    if (after >= 2) wait_vmcnt<2 * LPT>();
+    else if (after == 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    wait_lgkm0();
+    block_barrier();
+    if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1);
 
-    const bf16* kd = smem + st * 2 * TILE_ELEMS;
+    const int32_t kt0 = k_begin + it * KT;
+    const bf16* kd = smem + (it % NSTAGE) * STAGE_ELEMS;
     const bf16* vd = kd + TILE_ELEMS;
 
-    // S^T = K Q^T for the 4 sub-tiles of 16 keys.
-    f32x4 sacc[4];
+    // S^T = K Q^T for the two sub-tiles of 16 keys (all K fragments first).
+    bf16x8 kf[2][DS];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int row = 16 * t + m;
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds) {
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(kd + row * DH + swz<DH>(row, j + 4 * ds) * 8);
-        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ds], sacc[t], 0, 0, 0);
+        const int row = 16 * t + m;
+        kf[t][ds] = *reinterpret_cast<const bf16x8*>(kd + row * DH + swz_k<DH>(row, j + 4 * ds) * 8);
       }
+    f32x4 sacc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      sacc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        sacc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[t][ds], qf[ds], sacc[t], 0, 0, 0);
     }
 
-    // Online softmax on this lane's 16 keys (16t + 4j + i) of query row m.
+    // Online softmax on this lane's 8 keys (16t + 4j + i) of query row m.
     const bool need_mask = (kt0 + KT > k_end) ||
                            (a.causal && (kt0 + KT - 1 > qmin ||
                                          (a.window > 0 && kt0 <= qmax - a.window)));
-    float sv[4][4];
+    float sv[2][4];
     float tmax = -INFINITY;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float v = sacc[t][i] * a.scale_log2;
@@ -293,51 +360,51 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
         tmax = fmaxf(tmax, v);
       }
     tmax = xrow4_max(tmax);
-    const float mnew = fmaxf(mx, tmax);
-    const float msafe = (mnew == -INFINITY) ? 0.f : mnew;
-    const float alpha = fast_exp2(mx - msafe);
-    mx = mnew;
-    float psum = 0.f;
-    bf16x8 pf[2];
+    // Rescale only when some row's max outgrew the reference by > TAU; the
+    // exponentials stay <= 2^TAU otherwise. Exact: the same reference max is
+    // used for the sum and the accumulator.
+    if (__ballot(tmax > mx + TAU)) {
+      const float mnew = fmaxf(mx, tmax);
+      const float alpha = (mnew == -INFINITY) ? 1.f : fast_exp2(mx - mnew);
+      lsum *= alpha;
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+      for (int dt = 0; dt < DT; ++dt) acc_o[dt] = acc_o[dt] * alpha;
+      mx = mnew;
+    }
+    const float msafe = (mx == -INFINITY) ? 0.f : mx;
+    bf16x8 pf;
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float p = fast_exp2(sv[t][i] - msafe);
         psum += p;
-        pf[t >> 1][(t & 1) * 4 + i] = f2bf(p);
+        pf[4 * t + i] = f2bf(p);
       }
-    lsum = lsum * alpha + psum;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc_o[dt] = acc_o[dt] * alpha;
+    lsum += psum;
 
-    // O^T += V^T P^T over two 32-key steps. The transpose read hands lane i of
-    // group j the column (16dt + i) of rows key(j, e); source lane s supplies
-    // row 32ks + 16h + 4j + s/4, columns 16dt + 4(s%4) .. +3.
-    const int src_row = 4 * j + (m >> 2);
-    const int src_col4 = (m & 3) * 4;
+    // O^T += V^T P^T over the 32 keys. The transpose read hands lane i of
+    // group j column (16dt + i) of rows key(j, e); source lane s supplies row
+    // 16h + 4j + s/4 at columns 16dt + 4(s%4) .. +3.
+    bf16x8 vf[DT];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int dt = 0; dt < DT; ++dt) {
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt) {
-        bf16x8 vf;
+      for (int h = 0; h < 2; ++h) {
+        const int row = 16 * h + src_row;
+        const int col = 16 * dt + src_col4;
+        const int off = row * DH + swz_v<DH>(row, col >> 3) * 8 + (col & 7);
+        const i16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (DF_LDS i16x4*)((DF_LDS bf16*)(vd + off)));
+        const bf16x4 bv = __builtin_bit_cast(bf16x4, tv);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int row = 32 * ks + 16 * h + src_row;
-          const int col = 16 * dt + src_col4;
-          const int off = row * DH + swz<DH>(row, col >> 3) * 8 + (col & 7);
-          const i16x4 tv = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (DF_LDS i16x4*)((DF_LDS bf16*)(vd + off)));
-          const bf16x4 bv = __builtin_bit_cast(bf16x4, tv);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) vf[4 * h + e] = bv[e];
-        }
-        acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[ks], acc_o[dt], 0, 0, 0);
+        for (int e = 0; e < 4; ++e) vf[dt][4 * h + e] = bv[e];
       }
     }
-
-    if (has_next) store_tile(st ^ 1);
-    __syncthreads();
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      acc_o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], pf, acc_o[dt], 0, 0, 0);
   }
 
   const float ltot = xrow4_sum(lsum);
@@ -358,7 +425,8 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
-  // Split: publish the partial, then the last unit of (r, qt, g) merges.
+  // Split: publish the partial (unnormalised O, reference max, sum). The
+  // merge kernel that follows on the stream combines the splits.
   {
     float* po = a.part_o + ((int64_t)blockIdx.x * QROWS + nrow_unit) * DH + 4 * j;
 #pragma unroll
@@ -368,63 +436,99 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
       float2* pml = reinterpret_cast<float2*>(a.part_ml) + (int64_t)blockIdx.x * QROWS + nrow_unit;
       *pml = make_float2(mx, ltot);
     }
+    if (un.s == 0 && tid == 0)
+      a.dir[((int64_t)un.r * a.qtiles + un.qt) * a.hkv + g] = un.first;
   }
-  __shared__ int s_last;
-  __threadfence();
-  __syncthreads();
-  int32_t* ctr = a.counters + ((int64_t)un.r * a.qtiles + un.qt) * a.hkv + g;
-  if (tid == 0) s_last = (atomicAdd(ctr, 1) == un.nsplit - 1);
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
+}
 
-  // Merge: thread -> (row, quarter of the head dim); splits in index order.
-  const int row = tid >> 2;
-  const int dq = (tid & 3) * (DH / 4);
-  const int32_t nq2 = un.qt * QROWS + row;
-  float mmax = -INFINITY;
-  for (int32_t s = 0; s < un.nsplit; ++s) {
-    const int64_t slot = (int64_t)(un.first + s) * a.hkv + g;
-    const float2 ml = reinterpret_cast<const float2*>(a.part_ml)[slot * QROWS + row];
-    mmax = fmaxf(mmax, ml.x);
-  }
-  const float msafe = (mmax == -INFINITY) ? 0.f : mmax;
-  float o[DH / 4];
+// Merge of split partials: one workgroup per (request, query tile, kv-head,
+// block of MROWS rows); thread -> (row, 8 head-dim values). Splits are
+// consumed in index order by a streaming log-sum-exp, MB at a time with their
+// loads in flight, so the result does not depend on scheduling.
+constexpr int MROWS = 16;
+template <int DH>
+__global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a, int32_t units) {
+  constexpr int DV = 8;                   // head-dim values per thread
+  constexpr int TPR = DH / DV;            // threads per row
+  constexpr int RPW = NT / TPR;           // rows per workgroup pass
+  constexpr int MB = 4;
+  const int32_t rb_count = QROWS / MROWS;
+  int64_t id = blockIdx.x;
+  const int32_t rb = (int32_t)(id % rb_count); id /= rb_count;
+  const int32_t g = (int32_t)(id % a.hkv); id /= a.hkv;
+  const int32_t qt = (int32_t)(id % a.qtiles); id /= a.qtiles;
+  const int32_t r = (int32_t)id;
+  if (r >= a.num_reqs) return;
+  int32_t clen, blen, lo, ns, nq;
+  request_shape(a, r, &clen, &blen, &lo, &ns, &nq);
+  if (ns <= 1 || qt >= nq) return;  // unsplit units wrote their output directly
+  const int32_t first = a.dir[((int64_t)r * a.qtiles + qt) * a.hkv + g];
+  if (first < 0 || first + ns > units) return;
+  int32_t c0, c1, b0, b1;
+  request_rows(a.cu_ctx, a.cu_blk, r, a.total_ctx, a.total_blk, &c0, &c1, &b0, &b1);
+  const int32_t nrows = a.group * blen;
+  const int tid = threadIdx.x;
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
+  constexpr int PASSES = (MROWS + RPW - 1) / RPW;
 #pragma unroll
-  for (int d = 0; d < DH / 4; ++d) o[d] = 0.f;
-  float L = 0.f;
-  for (int32_t s = 0; s < un.nsplit; ++s) {
-    const int64_t slot = (int64_t)(un.first + s) * a.hkv + g;
-    const float2 ml = reinterpret_cast<const float2*>(a.part_ml)[slot * QROWS + row];
-    const float wgt = fast_exp2(ml.x - msafe);
-    L += ml.y * wgt;
-    const float* src = a.part_o + (slot * QROWS + row) * DH + dq;
+  for (int pass = 0; pass < PASSES; ++pass) {
+    const int rloc = pass * RPW + tid / TPR;
+    if (rloc >= MROWS) break;
+    const int row = rb * MROWS + rloc;
+    const int d0 = (tid % TPR) * DV;
+    const int32_t nq2 = qt * QROWS + row;
+    float o[DV];
 #pragma unroll
-    for (int d = 0; d < DH / 4; d += 4) {
-      const f32x4 v = *reinterpret_cast<const f32x4*>(src + d);
-      o[d] += v[0] * wgt;
-      o[d + 1] += v[1] * wgt;
-      o[d + 2] += v[2] * wgt;
-      o[d + 3] += v[3] * wgt;
+    for (int d = 0; d < DV; ++d) o[d] = 0.f;
+    float M = -INFINITY, L = 0.f;
+    for (int32_t s0 = 0; s0 < ns; s0 += MB) {
+      float2 ml[MB];
+      f32x4 ov[MB][DV / 4];
+#pragma unroll
+      for (int bb = 0; bb < MB; ++bb) {
+        const int32_t sidx = s0 + bb < ns ? s0 + bb : ns - 1;
+        const int64_t slot = (int64_t)(first + sidx) * a.hkv + g;
+        ml[bb] = pml[slot * QROWS + row];
+        const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + (slot * QROWS + row) * DH + d0);
+#pragma unroll
+        for (int d = 0; d < DV / 4; ++d) ov[bb][d] = src[d];
+      }
+      float bm = M;
+#pragma unroll
+      for (int bb = 0; bb < MB; ++bb)
+        if (s0 + bb < ns) bm = fmaxf(bm, ml[bb].x);
+      const float bsafe = (bm == -INFINITY) ? 0.f : bm;
+      const float rescale = fast_exp2(M - bsafe);
+      L *= rescale;
+#pragma unroll
+      for (int d = 0; d < DV; ++d) o[d] *= rescale;
+#pragma unroll
+      for (int bb = 0; bb < MB; ++bb) {
+        const float wgt = (s0 + bb < ns) ? fast_exp2(ml[bb].x - bsafe) : 0.f;
+        L += ml[bb].y * wgt;
+#pragma unroll
+        for (int d = 0; d < DV / 4; ++d) {
+          o[4 * d] += ov[bb][d][0] * wgt;
+          o[4 * d + 1] += ov[bb][d][1] * wgt;
+          o[4 * d + 2] += ov[bb][d][2] * wgt;
+          o[4 * d + 3] += ov[bb][d][3] * wgt;
+        }
+      }
+      M = bm;
     }
-  }
-  if (nq2 < nrows) {
-    const int32_t hl2 = nq2 / un.blen;
-    const int32_t b2 = nq2 - hl2 * un.blen;
-    const int64_t qrow2 = (int64_t)un.blk0 + b2;
-    if (qrow2 < a.total_blk) {
-      const float inv = L > 0.f ? 1.0f / L : 0.f;
-      bf16* dst = a.out + (qrow2 * a.hq + g * a.group + hl2) * DH + dq;
-#pragma unroll
-      for (int d = 0; d < DH / 4; d += 8) {
+    if (nq2 < nrows) {
+      const int32_t hl2 = nq2 / blen;
+      const int32_t b2 = nq2 - hl2 * blen;
+      const int64_t qrow2 = (int64_t)b0 + b2;
+      if (qrow2 < a.total_blk) {
+        const float inv = L > 0.f ? 1.0f / L : 0.f;
         bf16x8 v;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = f2bf(o[d + e] * inv);
-        *reinterpret_cast<bf16x8*>(dst + d) = v;
+        for (int e = 0; e < DV; ++e) v[e] = f2bf(o[e] * inv);
+        *reinterpret_cast<bf16x8*>(a.out + (qrow2 * a.hq + g * a.group + hl2) * DH + d0) = v;
       }
     }
   }
-  if (tid == 0) *ctr = 0;  // leave the ticket zeroed for the next call
 }
 
 // ----------------------------------------------------------------------------
@@ -554,9 +658,18 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPl
   if (p.split_keys > 0) {
     pl.chunk = p.split_keys;
   } else {
-    const int64_t target = 2LL * (num_cus > 0 ? num_cus : 256);
+    // Resident workgroup slots (two per compute unit at this kernel's LDS use).
+    // If every (request, query tile, kv-head) can have a few units, size the
+    // units so the whole grid is resident at once (no partial second round);
+    // otherwise cut the keys into units of a few rounds' worth.
+    const int64_t slots = 2LL * (num_cus > 0 ? num_cus : 256);
+    const int64_t base = (int64_t)p.num_reqs * p.num_kv_heads * pl.qtiles;
     const int64_t work = eff * p.num_kv_heads * pl.qtiles;
-    int64_t c = (work + target - 1) / target;
+    int64_t c;
+    if (2 * base <= slots)
+      c = (work + (slots - base) - 1) / (slots - base);
+    else
+      c = (work + 4 * slots - 1) / (4 * slots);
     c = (c + KT - 1) / KT * KT;
     if (c < 128) c = 128;
     if (c > (1 << 20)) c = 1 << 20;
@@ -599,7 +712,7 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.q = (const bf16*)q; a.kb = (const bf16*)kb; a.vb = (const bf16*)vb;
   a.kc = (const bf16*)kc; a.vc = (const bf16*)vc; a.out = (bf16*)out;
   char* w = (char*)ws;
-  a.counters = (int32_t*)(w + plan.off_counters);
+  a.dir = (int32_t*)(w + plan.off_counters);
   a.part_o = (float*)(w + plan.off_part_o);
   a.part_ml = (float*)(w + plan.off_part_ml);
   a.total_ctx = p.total_ctx; a.total_blk = p.total_blk;
@@ -609,15 +722,27 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.scale_log2 = p.scale * LOG2E;
   a.causal = p.causal ? 1 : 0; a.window = p.window;
   const int64_t blocks = plan.units * p.num_kv_heads;
-  const size_t lds = 2 * 2 * (size_t)KT * p.head_dim * sizeof(bf16);
+  const size_t lds = (size_t)NSTAGE * 2 * KT * p.head_dim * sizeof(bf16);
+  // The LDS limit attribute is a per-function setting: raise it once per
+  // device (not per launch, so that stream capture sees only the launch).
+  static std::once_flag once[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::call_once(once[dev & 63], [] {
+    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2);
+    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64>,
+                        hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2);
+  });
+  const int64_t mblocks = (int64_t)p.num_reqs * plan.qtiles * p.num_kv_heads * (QROWS / MROWS);
   if (p.head_dim == 128) {
-    hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(block_attn_bf16_kernel<128>, dim3((unsigned)blocks), dim3(NT), lds, s, a);
+    hipLaunchKernelGGL(block_attn_merge_kernel<128>, dim3((unsigned)mblocks), dim3(NT), 0, s, a,
+                       (int32_t)plan.units);
   } else {
-    hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     hipLaunchKernelGGL(block_attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(NT), lds, s, a);
+    hipLaunchKernelGGL(block_attn_merge_kernel<64>, dim3((unsigned)mblocks), dim3(NT), 0, s, a,
+                       (int32_t)plan.units);
   }
   return hipGetLastError();
 }

@@ -148,9 +148,9 @@ dflash_status dflash_block_attention_check(const dflash_block_attn_params* p);
  *   k_ctx   [total_ctx, Hkv, Dh], v_ctx alike; may be NULL if total_ctx == 0.
  *   out     [total_blk, Hq, Dh], written (rows of empty requests untouched).
  *   workspace  device, 256-byte aligned, >= dflash_block_attention_workspace_size
- *           bytes, ZERO-FILLED before its first use; every call leaves it
- *           zero-filled again where it must be. One workspace must not be used
- *           by two calls that may run concurrently.
+ *           bytes (no initialisation needed). It holds the f32 partial results
+ *           of key ranges that were split across work units; one workspace must
+ *           not be used by two calls that may run concurrently.
  * The result does not depend on how the keys are split into work units other
  * than through f32 rounding; for a fixed split_keys it is bitwise
  * deterministic.

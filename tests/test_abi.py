@@ -1,0 +1,133 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, the ctypes struct matches the C layout, and host-side
+validation returns the documented status codes. No compute entry point is
+called here."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from block_diffusion_draft_dflash_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z0-9_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        pytest.fail("libdflash.so is not built (run __graft_entry__.build())")
+    return B.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert names, "no declarations parsed"
+    assert sorted(B.EXPORTED) == names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_error_string(lib):
+    assert lib.dflash_abi_version() == 100
+    assert isinstance(lib.dflash_last_error(), bytes)
+
+
+def test_struct_layout_matches_c(tmp_path):
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "layout.c"
+    src.write_text(
+        '#include <stdio.h>\n#include <stddef.h>\n#include "dflash.h"\n'
+        "int main(void){printf(\"%zu\", sizeof(dflash_block_attn_params));"
+        + "".join(f'printf(" %zu", offsetof(dflash_block_attn_params, {f}));'
+                  for f, _ in B.BlockAttnParams._fields_)
+        + "return 0;}\n")
+    exe = tmp_path / "layout"
+    subprocess.check_call([gcc, "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    vals = [int(x) for x in subprocess.check_output([str(exe)]).split()]
+    assert vals[0] == ctypes.sizeof(B.BlockAttnParams)
+    for (f, _), off in zip(B.BlockAttnParams._fields_, vals[1:]):
+        assert getattr(B.BlockAttnParams, f).offset == off, f
+
+
+def P(**kw):
+    base = dict(num_reqs=8, num_q_heads=32, num_kv_heads=8, head_dim=128, dtype=B.DFLASH_BF16,
+                total_ctx=10000, total_blk=128, max_blk_len=16, scale=128 ** -0.5, causal=False,
+                window=0, split_keys=0)
+    base.update(kw)
+    return B.make_block_attn_params(**base)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(), B.DFLASH_OK),
+    (dict(dtype=B.DFLASH_F32), B.DFLASH_OK),
+    (dict(num_reqs=0), B.DFLASH_ERR_INVALID_ARG),
+    (dict(num_q_heads=30), B.DFLASH_ERR_INVALID_ARG),
+    (dict(num_kv_heads=0), B.DFLASH_ERR_INVALID_ARG),
+    (dict(head_dim=96), B.DFLASH_ERR_UNSUPPORTED),
+    (dict(head_dim=63), B.DFLASH_ERR_INVALID_ARG),
+    (dict(dtype=7), B.DFLASH_ERR_INVALID_ARG),
+    (dict(total_ctx=-1), B.DFLASH_ERR_INVALID_ARG),
+    (dict(max_blk_len=200), B.DFLASH_ERR_INVALID_ARG),
+    (dict(max_blk_len=0), B.DFLASH_ERR_INVALID_ARG),
+    (dict(window=64), B.DFLASH_ERR_INVALID_ARG),          # window without causal
+    (dict(window=64, causal=True), B.DFLASH_OK),
+    (dict(window=-1, causal=True), B.DFLASH_ERR_INVALID_ARG),
+    (dict(split_keys=100), B.DFLASH_ERR_INVALID_ARG),
+    (dict(split_keys=128), B.DFLASH_OK),
+    (dict(scale=float("nan")), B.DFLASH_ERR_INVALID_ARG),
+    (dict(total_ctx=2 ** 30), B.DFLASH_ERR_INVALID_ARG),
+    (dict(total_ctx=0), B.DFLASH_OK),
+    (dict(total_blk=0, max_blk_len=0), B.DFLASH_OK),
+])
+def test_block_attention_validation(lib, kw, status):
+    p = P(**kw)
+    assert B.dflash_block_attention_check(p) == status, B.dflash_last_error()
+    if status != B.DFLASH_OK:
+        assert B.dflash_last_error()
+        assert B.dflash_block_attention_workspace_size(p) == 0
+
+
+def test_workspace_sizes(lib):
+    bf = B.dflash_block_attention_workspace_size(P())
+    assert bf > 0 and bf % 256 == 0
+    # f32 runs unsplit and needs no workspace
+    assert B.dflash_block_attention_workspace_size(P(dtype=B.DFLASH_F32)) == 0
+    # more context -> at least as much workspace; forced small splits -> more
+    assert B.dflash_block_attention_workspace_size(P(total_ctx=100000)) >= bf
+    assert B.dflash_block_attention_workspace_size(P(split_keys=64)) > \
+        B.dflash_block_attention_workspace_size(P(split_keys=4096))
+    # the plan is a pure function of the parameters
+    assert B.dflash_block_attention_workspace_size(P()) == bf
+
+
+def test_context_kv_workspace_size(lib):
+    n = B.dflash_context_kv_workspace_size(131072, 4096, 8, 128)
+    assert n >= 2 * 1024 * 4096 * 2 + 131072 * 4
+    assert B.dflash_context_kv_workspace_size(-1, 4096, 8, 128) == 0
+
+
+def test_binding_requires_library(tmp_path):
+    with pytest.raises(RuntimeError):
+        B.load.__wrapped__(str(tmp_path / "missing.so")) if hasattr(B.load, "__wrapped__") else \
+            _load_fresh(str(tmp_path / "missing.so"))
+
+
+def _load_fresh(path):
+    saved = B._lib
+    B._lib = None
+    try:
+        return B.load(path)
+    finally:
+        B._lib = saved
