@@ -109,6 +109,9 @@ def main() -> int:
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--copy-calibration-mb", type=int, default=0,
+                    help="before timing, run a plain device copy of this many MiB (3 times) so a "
+                         "counter profile of the same run can scale FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -125,6 +128,14 @@ def main() -> int:
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
     B.load()
+    if args.copy_calibration_mb > 0:
+        n = args.copy_calibration_mb << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     wl = make_workload(args.workload)
     paths = [DevicePath(wl, split_keys=args.split_keys) for _ in range(args.rotate)]
     for p in paths:

@@ -247,9 +247,18 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
     koff[i] = lrow[i] * rstride + swz_k<DH>(lrow[i], lane % CH) * 8;
     voff[i] = lrow[i] * rstride + swz_v<DH>(lrow[i], lane % CH) * 8;
   }
+  // The copies are issued through inline assembly: the compiler's wait
+  // insertion cannot tell which LDS stage a later LDS read touches and would
+  // otherwise drain every copy in flight before it. All waits on these copies
+  // are explicit (wait_vmcnt below); no other vector-memory load is in flight
+  // while they are.
   auto dma = [](const bf16* src, bf16* dst) {
-    __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                     (DF_LDS void*)dst, 16, 0, 0);
+    const uint32_t lds_addr =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_addr), "v"(src)
+                 : "memory", "m0");
   };
   auto issue_tile = [&](int32_t t) {
     const int32_t kt0 = k_begin + t * KT;
@@ -299,6 +308,9 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int t = 0; t < NSTAGE - 1; ++t)
     if (t < ntiles) issue_tile(t);
+  // Settle the q fragments (and the prologue copies) once, before the loop;
+  // inside it the only vector-memory operations are the tile copies.
+  wait_vmcnt<0>();
 
   const int src_row = 4 * j + (m >> 2);
   const int src_col4 = (m & 3) * 4;
