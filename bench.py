@@ -1,10 +1,12 @@
 #!/usr/bin/env python3
 """Benchmark of the DFlash draft block-attention hot path on one MI355X.
 
-One step = one pass of the path over one synthetic batch: the fused per-head
-q/k RMSNorm + NeoX RoPE of the block rows (``dflash_qk_norm_rope``), then the
-block attention over [context; block] (``dflash_block_attention``: work-unit
-lookup, MFMA attention, split merge). The context keys are prepared once
+One step = one pass of the path over one synthetic batch: the per-head q/k
+RMSNorm + NeoX RoPE of the block rows and the block attention over
+[context; block], as one ``dflash_block_attention`` call with the fused
+prologue (work-unit lookup, norm + RoPE, MFMA attention, split merge).
+``--unfused`` runs ``dflash_qk_norm_rope`` in place first and the attention
+on the normed rows (two calls). The context keys are prepared once
 before timing (``dflash_context_kv`` / K-only ``dflash_qk_norm_rope``), as a
 serving engine does when it appends context rows.
 
@@ -108,6 +110,8 @@ def main() -> int:
     ap.add_argument("--rotate", type=int, default=12, help="copies of the batch cycled per step")
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
+    ap.add_argument("--unfused", action="store_true",
+                    help="q/k norm + RoPE as a separate in-place call before the attention")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB (3 times) so a "
@@ -143,10 +147,14 @@ def main() -> int:
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
+    fused = wl.dtype == "bf16" and not args.unfused
+
     def run_steps(n, attention_only=False):
         for i in range(n):
             p = paths[i % len(paths)]
-            if attention_only:
+            if fused:
+                p.step_fused()          # the step is the attention call
+            elif attention_only:
                 p.attention()
             else:
                 p.step()
@@ -240,11 +248,13 @@ def main() -> int:
             "mask": ("causal, window %d" % wl.window) if wl.causal else "bidirectional",
             "rotating_copies": len(paths),
             "hip_graph": use_graph,
+            "fused_qk_norm_rope": fused,
         },
         "draft_query_tokens_per_s": tokens_per_s,
         "roofline": {
             "bound": "hbm",
-            "kernel": "block_attn_bf16_kernel",
+            "kernel": ("dflash_block_attention call = block_attn_bf16_kernel%s + "
+                       "block_attn_merge_kernel" % (" (fused q/k norm + RoPE)" if fused else "")),
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

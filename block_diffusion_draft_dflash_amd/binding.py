@@ -63,6 +63,19 @@ class BlockAttnParams(ctypes.Structure):
     ]
 
 
+class QkPrologue(ctypes.Structure):
+    """Mirror of ``dflash_qk_prologue`` (fused q/k norm + RoPE of the attention)."""
+
+    _fields_ = [
+        ("q_norm_w", ctypes.c_void_p),
+        ("k_norm_w", ctypes.c_void_p),
+        ("positions", ctypes.c_void_p),
+        ("rope_table", ctypes.c_void_p),
+        ("max_pos", ctypes.c_int32),
+        ("eps", ctypes.c_float),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -90,7 +103,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dflash_block_attention_check.restype = ctypes.c_int
     lib.dflash_block_attention_check.argtypes = [ctypes.POINTER(BlockAttnParams)]
     lib.dflash_block_attention.restype = ctypes.c_int
-    lib.dflash_block_attention.argtypes = [ctypes.POINTER(BlockAttnParams), P, P, P, P, P, P, P, P,
+    lib.dflash_block_attention.argtypes = [ctypes.POINTER(BlockAttnParams),
+                                           ctypes.POINTER(QkPrologue), P, P, P, P, P, P, P, P,
                                            P, SZ, P]
     lib.dflash_context_kv_workspace_size.restype = SZ
     lib.dflash_context_kv_workspace_size.argtypes = [I64, I32, I32, I32]
@@ -173,14 +187,25 @@ def dflash_block_attention_workspace_size(p: BlockAttnParams) -> int:
     return load().dflash_block_attention_workspace_size(ctypes.byref(p))
 
 
+def make_qk_prologue(q_norm_w: torch.Tensor, k_norm_w: torch.Tensor, positions: torch.Tensor,
+                     rope_table: torch.Tensor, eps: float) -> QkPrologue:
+    return QkPrologue(_ptr(q_norm_w), _ptr(k_norm_w), _ptr(positions), _ptr(rope_table),
+                      rope_table.shape[0], float(eps))
+
+
 def dflash_block_attention(p: BlockAttnParams, cu_ctx_lens: torch.Tensor,
                            cu_blk_lens: torch.Tensor, q: torch.Tensor, k_blk: torch.Tensor,
                            v_blk: torch.Tensor, k_ctx: Optional[torch.Tensor],
                            v_ctx: Optional[torch.Tensor], out: torch.Tensor,
-                           workspace: Optional[torch.Tensor], stream=None) -> None:
+                           workspace: Optional[torch.Tensor], stream=None,
+                           prologue: Optional[QkPrologue] = None) -> None:
+    """Block attention; with ``prologue`` q and k_blk are raw and get q/k norm +
+    RoPE inside the kernel (they are not modified)."""
     lib = load()
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(lib.dflash_block_attention(ctypes.byref(p), _ptr(cu_ctx_lens), _ptr(cu_blk_lens),
+    _check(lib.dflash_block_attention(ctypes.byref(p),
+                                      ctypes.byref(prologue) if prologue is not None else None,
+                                      _ptr(cu_ctx_lens), _ptr(cu_blk_lens),
                                       _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_ctx), _ptr(v_ctx),
                                       _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
 

@@ -24,6 +24,7 @@
 //   (unnormalised O, running max, sum); the last unit to finish (integer
 //   ticket per (request, query tile, kv-head)) merges them in split order, so
 //   the result is deterministic.
+#include <algorithm>
 #include <mutex>
 
 #include "dflash_device.h"
@@ -50,14 +51,24 @@ struct AttnArgs {
   float* part_ml;     // [units * hkv][QROWS][2]
   int32_t* dir;       // [R][qtiles][hkv]: first unit index of each split set
   int64_t total_ctx, total_blk;
-  int32_t num_reqs, hq, hkv, group, chunk, qtiles, max_blk;
+  int32_t* hdr;       // workspace header: [0] = keys per split chosen for this call
+  int32_t num_reqs, hq, hkv, group, qtiles, max_blk;
+  int32_t chunk;      // keys per split (multiple of KT), or 0: chosen on the device
+  int32_t units;      // work units per kv-head in the grid (grid = units * hkv)
+  // Fused q/k prologue (q and k_blk raw): per-head RMSNorm + NeoX RoPE.
+  const float* qnw;     // [Dh]
+  const float* knw;     // [Dh]
+  const int32_t* bpos;  // [total_blk] positions of the block rows
+  const float2* rope;   // [max_pos][Dh/2] (cos, sin)
+  int32_t max_pos;
+  float eps;
   float scale_log2;
   int32_t causal, window;
 };
 
 struct Unit {
   int32_t r, qt, s, nsplit, first;  // first = global unit index of split 0 of this (r, qt)
-  int32_t clen, blen, lo;
+  int32_t clen, blen, lo, csz;      // csz = keys per split of this request
   int32_t ctx0, blk0;
 };
 
@@ -75,60 +86,132 @@ __device__ __forceinline__ void request_rows(const int32_t* cu_ctx, const int32_
   *b1 = min(max(cu_blk[r + 1], *b0), tb);
 }
 
-// Lengths of request r and its unit count (0 if the request has no block rows).
-__device__ __forceinline__ void request_shape(const AttnArgs& a, int32_t r, int32_t* clen,
-                                              int32_t* blen, int32_t* lo, int32_t* ns,
-                                              int32_t* nq) {
-  int32_t c0, c1, b0, b1;
-  request_rows(a.cu_ctx, a.cu_blk, r, a.total_ctx, a.total_blk, &c0, &c1, &b0, &b1);
-  *clen = c1 - c0;
-  *blen = min(b1 - b0, a.max_blk);
-  *lo = (a.causal && a.window > 0) ? clamp_nonneg(*clen - a.window + 1) : 0;
-  const int32_t n = *clen + *blen - *lo;
-  *ns = *blen > 0 ? (n + a.chunk - 1) / a.chunk : 0;
-  *nq = *blen > 0 ? (a.group * *blen + QROWS - 1) / QROWS : 0;
+// Lengths of one request as a lane holds them: first rows, context and block
+// lengths, first visible key, number of visible keys, query tiles.
+struct LaneReq {
+  int32_t c0, b0, clen, blen, lo, n, nq;
+};
+__device__ __forceinline__ LaneReq lane_req(const AttnArgs& a, int32_t r) {
+  LaneReq q{};
+  if (r >= a.num_reqs) return q;
+  int32_t c1, b1;
+  request_rows(a.cu_ctx, a.cu_blk, r, a.total_ctx, a.total_blk, &q.c0, &c1, &q.b0, &b1);
+  q.clen = c1 - q.c0;
+  q.blen = min(b1 - q.b0, a.max_blk);
+  q.lo = (a.causal && a.window > 0) ? clamp_nonneg(q.clen - a.window + 1) : 0;
+  q.n = q.blen > 0 ? q.clen + q.blen - q.lo : 0;
+  q.nq = q.blen > 0 ? (a.group * q.blen + QROWS - 1) / QROWS : 0;
+  return q;
+}
+// The key range [lo, clen + blen) of a request is cut into ns = ceil(n / chunk)
+// splits of equal size csz (rounded up to whole tiles); since chunk is a
+// multiple of the tile, the last split is never empty.
+__device__ __forceinline__ int32_t req_splits(const LaneReq& q, int32_t chunk) {
+  return q.n > 0 ? (q.n + chunk - 1) / chunk : 0;
+}
+__device__ __forceinline__ int32_t req_split_size(const LaneReq& q, int32_t ns) {
+  return ns > 0 ? ((q.n + ns - 1) / ns + KT - 1) / KT * KT : 0;
 }
 
-// Find work unit u by a wave-wide prefix scan over the requests' unit counts.
-// Every wave of the workgroup computes the same answer from the same data.
-__device__ bool find_unit(const AttnArgs& a, int32_t u, Unit* out) {
+__device__ __forceinline__ int32_t wave_sum(int32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+__device__ __forceinline__ int32_t wave_max(int32_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// The requests, 64 per lane group. Up to 64 requests they are loaded once and
+// kept in registers; beyond that each group is re-read when needed.
+struct ReqView {
+  const AttnArgs& a;
+  LaneReq cached;
+  __device__ ReqView(const AttnArgs& args) : a(args) {
+    cached = lane_req(a, threadIdx.x & 63);
+  }
+  __device__ __forceinline__ LaneReq group(int32_t r0) const {
+    return r0 == 0 ? cached : lane_req(a, r0 + (threadIdx.x & 63));
+  }
+};
+
+// Keys per split for this call. With a fixed split size requested, that one;
+// otherwise the smallest multiple of KT whose total unit count fits the
+// launched grid (a.units per kv-head), so that the grid is one balanced round
+// of equal-sized units. Every workgroup computes the same value from the same
+// lengths. The host guarantees a.units >= sum of nq_r, i.e. one unit per
+// (request, query tile) always fits.
+__device__ int32_t choose_chunk(const AttnArgs& a, const ReqView& rv) {
+  if (a.chunk > 0) return a.chunk;
+  auto count = [&](int32_t c) {
+    int32_t tot = 0;
+    for (int32_t r0 = 0; r0 < a.num_reqs; r0 += 64) {
+      const LaneReq q = rv.group(r0);
+      tot += wave_sum(req_splits(q, c) * q.nq);
+    }
+    return tot;
+  };
+  int32_t maxn = 0, work = 0;
+  for (int32_t r0 = 0; r0 < a.num_reqs; r0 += 64) {
+    const LaneReq q = rv.group(r0);
+    maxn = max(maxn, wave_max(q.n));
+    work += wave_sum(((q.n + KT - 1) / KT) * q.nq);  // in tiles
+  }
+  const int32_t kmax = max(1, (maxn + KT - 1) / KT);
+  int32_t klo = max(1, min(kmax, (work + a.units - 1) / max(a.units, 1)));
+  if (count(klo * KT) <= a.units) return klo * KT;
+  // grow geometrically, then bisect: count() is non-increasing in c
+  int32_t khi = klo, step = 1;
+  while (khi < kmax) {
+    khi = min(kmax, khi + step);
+    step *= 2;
+    if (count(khi * KT) <= a.units) break;
+    klo = khi;
+  }
+  while (khi - klo > 1) {
+    const int32_t mid = (klo + khi) / 2;
+    if (count(mid * KT) <= a.units) khi = mid; else klo = mid;
+  }
+  return khi * KT;
+}
+
+// Find work unit u (for split size `chunk`) by a wave-wide prefix scan over
+// the requests' unit counts; the owning lane's values are read back with
+// readlane. Every wave of the workgroup computes the same answer.
+__device__ bool find_unit(const AttnArgs& a, const ReqView& rv, int32_t chunk, int32_t u,
+                          Unit* out) {
   const int lane = threadIdx.x & 63;
   int32_t base = 0;
   for (int32_t r0 = 0; r0 < a.num_reqs; r0 += 64) {
-    const int32_t r = r0 + lane;
-    int32_t cnt = 0;
-    if (r < a.num_reqs) {
-      int32_t cl, bl, lo, ns, nq;
-      request_shape(a, r, &cl, &bl, &lo, &ns, &nq);
-      cnt = ns * nq;
-    }
+    const LaneReq q = rv.group(r0);
+    const int32_t ns = req_splits(q, chunk);
+    const int32_t cnt = ns * q.nq;
     int32_t incl = cnt;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
       const int32_t t = __shfl_up(incl, off, 64);
       if (lane >= off) incl += t;
     }
-    const int32_t total = __shfl(incl, 63, 64);
+    const int32_t total = __builtin_amdgcn_readlane(incl, 63);
     if (u < base + total) {
       const unsigned long long hit = __ballot(base + incl > u);
       const int idx = __ffsll((long long)hit) - 1;
-      const int32_t rr = r0 + idx;
-      const int32_t start = base + __shfl(incl - cnt, idx, 64);
-      int32_t cl, bl, lo, ns, nq;
-      request_shape(a, rr, &cl, &bl, &lo, &ns, &nq);
+      const int32_t start = base + __builtin_amdgcn_readlane(incl - cnt, idx);
+      const int32_t nsr = __builtin_amdgcn_readlane(ns, idx);
       const int32_t loc = u - start;
-      out->r = rr;
-      out->qt = loc / ns;
-      out->s = loc % ns;
-      out->nsplit = ns;
-      out->first = start + out->qt * ns;
-      out->clen = cl;
-      out->blen = bl;
-      out->lo = lo;
-      int32_t c0, c1, b0, b1;
-      request_rows(a.cu_ctx, a.cu_blk, rr, a.total_ctx, a.total_blk, &c0, &c1, &b0, &b1);
-      out->ctx0 = c0;
-      out->blk0 = b0;
+      out->r = r0 + idx;
+      out->qt = loc / nsr;
+      out->s = loc % nsr;
+      out->nsplit = nsr;
+      out->first = start + out->qt * nsr;
+      out->clen = __builtin_amdgcn_readlane(q.clen, idx);
+      out->blen = __builtin_amdgcn_readlane(q.blen, idx);
+      out->lo = __builtin_amdgcn_readlane(q.lo, idx);
+      out->csz = __builtin_amdgcn_readlane(req_split_size(q, ns), idx);
+      out->ctx0 = __builtin_amdgcn_readlane(q.c0, idx);
+      out->blk0 = __builtin_amdgcn_readlane(q.b0, idx);
       return true;
     }
     base += total;
@@ -173,7 +256,57 @@ __device__ __forceinline__ void block_barrier() {
 
 constexpr int NSTAGE = 4;  // LDS stages: NSTAGE - 1 tiles in flight
 
+// Per-head RMSNorm + NeoX RoPE of one head vector held by the four lanes
+// {m, m+16, m+32, m+48} in the MFMA operand layout: this lane holds chunks
+// j + 4 ds (ds < DS) of 8 elements, i.e. d = 8 (j + 4 ds) + e; chunk ds pairs
+// with chunk ds + DS/2 (d and d + Dh/2). Same arithmetic as qk_norm_rope_kernel:
+// y = x * (1/rms) * w, then (y_lo c - y_hi s, y_hi c + y_lo s), rounded once.
 template <int DH>
+__device__ __forceinline__ void norm_rope_frag(const bf16x8 (&xin)[DH / 32], const float* w,
+                                               const float2* cs, float eps, int j,
+                                               bf16x8 (&out)[DH / 32]) {
+  constexpr int DS = DH / 32;
+  float x[DS][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int ds = 0; ds < DS; ++ds)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      x[ds][e] = bf2f(xin[ds][e]);
+      ss += x[ds][e] * x[ds][e];
+    }
+  ss = xrow4_sum(ss);
+  const float inv = 1.0f / sqrtf(ss * (1.0f / DH) + eps);
+#pragma unroll
+  for (int ds = 0; ds < DS / 2; ++ds) {
+    const int dlo = 8 * (j + 4 * ds);
+    const float4* wl = reinterpret_cast<const float4*>(w + dlo);
+    const float4* wh = reinterpret_cast<const float4*>(w + dlo + DH / 2);
+    const float4* c4 = reinterpret_cast<const float4*>(cs + dlo);
+    const float4 wl0 = wl[0], wl1 = wl[1], wh0 = wh[0], wh1 = wh[1];
+    const float wlo[8] = {wl0.x, wl0.y, wl0.z, wl0.w, wl1.x, wl1.y, wl1.z, wl1.w};
+    const float whi[8] = {wh0.x, wh0.y, wh0.z, wh0.w, wh1.x, wh1.y, wh1.z, wh1.w};
+    float c[8], sn[8];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float4 v = c4[h];
+      c[2 * h] = v.x; sn[2 * h] = v.y; c[2 * h + 1] = v.z; sn[2 * h + 1] = v.w;
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float lo = x[ds][e] * inv * wlo[e];
+      const float hi = x[ds + DS / 2][e] * inv * whi[e];
+      out[ds][e] = f2bf(lo * c[e] - hi * sn[e]);
+      out[ds + DS / 2][e] = f2bf(hi * c[e] + lo * sn[e]);
+    }
+  }
+}
+
+__device__ __forceinline__ int32_t clamp_pos(int32_t p, int32_t max_pos) {
+  return p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+}
+
+template <int DH, bool FUSE>
 __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
   constexpr int CH = DH / 8;                 // 16-byte chunks per row
   constexpr int DS = DH / 32;                // MFMA k-steps over the head dim
@@ -188,12 +321,16 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
 
   const int32_t g = blockIdx.x % a.hkv;
   const int32_t u = blockIdx.x / a.hkv;
+  const ReqView rv(a);
+  const int32_t chunk = __builtin_amdgcn_readfirstlane(choose_chunk(a, rv));
+  if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[0] = chunk;  // for the merge kernel
   Unit un;
-  if (!find_unit(a, u, &un)) return;  // uniform over the workgroup
+  if (!find_unit(a, rv, chunk, u, &un)) return;  // uniform over the workgroup
   // Every lane holds the same unit; say so to the compiler (scalar registers,
   // scalar branches).
   un.r = uni(un.r); un.qt = uni(un.qt); un.s = uni(un.s); un.nsplit = uni(un.nsplit);
   un.first = uni(un.first); un.clen = uni(un.clen); un.blen = uni(un.blen); un.lo = uni(un.lo);
+  un.csz = uni(un.csz);
   un.ctx0 = uni(un.ctx0); un.blk0 = uni(un.blk0);
 
   const int tid = threadIdx.x;
@@ -203,8 +340,8 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
   const int j = lane >> 4;   // lane group
 
   const int32_t n_all = un.clen + un.blen;
-  const int32_t k_begin = un.lo + un.s * a.chunk;
-  const int32_t k_end = min(k_begin + a.chunk, n_all);
+  const int32_t k_begin = un.lo + un.s * un.csz;
+  const int32_t k_end = min(k_begin + un.csz, n_all);
   const int32_t ntiles = (k_end - k_begin + KT - 1) / KT;
 
   // This lane's query row.
@@ -216,6 +353,27 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
   const bool rvalid = nq < nrows && qrow < a.total_blk;
   const int32_t qhead = g * a.group + hl;
   const int32_t qidx = un.clen + b;  // index of this query in [context; block]
+
+  // With the fused prologue the tiles that hold block keys are visited first
+  // (the softmax is order-free), so their K rows can be normalised in LDS
+  // before the loop. kb_first / nblk: the unit's block rows.
+  const int32_t kb_first = max(k_begin, un.clen);
+  const int32_t nblk = FUSE ? max(0, k_end - kb_first) : 0;
+  const int32_t rot = nblk > 0 ? (kb_first - k_begin) / KT : 0;
+  auto tile_k0 = [&](int32_t it) {
+    int32_t t = it + rot;
+    if (t >= ntiles) t -= ntiles;
+    return k_begin + t * KT;
+  };
+
+  // Positions needed by the fused prologue: this lane's query row and the
+  // block K row (16 w + m) it normalises.
+  const int32_t krho = 16 * w + m;
+  int32_t pos_q = 0, pos_k = 0;
+  if constexpr (FUSE) {
+    if (rvalid) pos_q = clamp_pos(a.bpos[qrow], a.max_pos);
+    if (krho < nblk) pos_k = clamp_pos(a.bpos[(int64_t)un.blk0 + (kb_first - un.clen) + krho], a.max_pos);
+  }
 
   bf16x8 qf[DS];
 #pragma unroll
@@ -261,7 +419,7 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
                  : "memory", "m0");
   };
   auto issue_tile = [&](int32_t t) {
-    const int32_t kt0 = k_begin + t * KT;
+    const int32_t kt0 = tile_k0(t);
     bf16* st = smem + (t % NSTAGE) * STAGE_ELEMS;
     if (kt0 + KT <= min(un.clen, k_end)) {
       const int64_t base = (int64_t)(un.ctx0 + kt0) * rstride;
@@ -312,6 +470,37 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
   // inside it the only vector-memory operations are the tile copies.
   wait_vmcnt<0>();
 
+  if constexpr (FUSE) {
+    // q: RMSNorm + RoPE in registers (rows of this lane group).
+    const float2* csq = a.rope + (int64_t)pos_q * (DH / 2);
+    bf16x8 qn[DS];
+    norm_rope_frag<DH>(qf, a.qnw, csq, a.eps, j, qn);
+#pragma unroll
+    for (int ds = 0; ds < DS; ++ds) qf[ds] = rvalid ? qn[ds] : bf16x8{};
+    // block K rows: in place in the LDS stages of the first tiles (at most
+    // NSTAGE - 1 of them hold block keys: max_blk_len <= 2 KT is required).
+    if (nblk > 0) {
+      wait_lgkm0();
+      block_barrier();
+      const bool kv = krho < nblk;
+      const int32_t kidx = kb_first + (kv ? krho : 0);
+      const int32_t itk = (kidx - k_begin) / KT - rot;  // iteration that holds it
+      const int row = (kidx - k_begin) % KT;
+      bf16* kr = smem + itk * STAGE_ELEMS + row * DH;
+      bf16x8 kx[DS], ky[DS];
+#pragma unroll
+      for (int ds = 0; ds < DS; ++ds)
+        kx[ds] = kv ? *reinterpret_cast<const bf16x8*>(kr + swz_k<DH>(row, j + 4 * ds) * 8) : bf16x8{};
+      const float2* csk = a.rope + (int64_t)pos_k * (DH / 2);
+      norm_rope_frag<DH>(kx, a.knw, csk, a.eps, j, ky);
+      if (kv) {
+#pragma unroll
+        for (int ds = 0; ds < DS; ++ds)
+          *reinterpret_cast<bf16x8*>(kr + swz_k<DH>(row, j + 4 * ds) * 8) = ky[ds];
+      }
+    }
+  }
+
   const int src_row = 4 * j + (m >> 2);
   const int src_col4 = (m & 3) * 4;
 
@@ -326,7 +515,7 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
     block_barrier();
     if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1);
 
-    const int32_t kt0 = k_begin + it * KT;
+    const int32_t kt0 = tile_k0(it);
     const bf16* kd = smem + (it % NSTAGE) * STAGE_ELEMS;
     const bf16* vd = kd + TILE_ELEMS;
 
@@ -459,7 +648,7 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
 // loads in flight, so the result does not depend on scheduling.
 constexpr int MROWS = 16;
 template <int DH>
-__global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a, int32_t units) {
+__global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
   constexpr int DV = 8;                   // head-dim values per thread
   constexpr int TPR = DH / DV;            // threads per row
   constexpr int RPW = NT / TPR;           // rows per workgroup pass
@@ -471,13 +660,15 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a, int32_
   const int32_t qt = (int32_t)(id % a.qtiles); id /= a.qtiles;
   const int32_t r = (int32_t)id;
   if (r >= a.num_reqs) return;
-  int32_t clen, blen, lo, ns, nq;
-  request_shape(a, r, &clen, &blen, &lo, &ns, &nq);
-  if (ns <= 1 || qt >= nq) return;  // unsplit units wrote their output directly
+  // The split size (chosen by the main kernel of this call unless fixed), the
+  // directory entry and the lengths are independent loads.
+  const int32_t chunk = a.chunk > 0 ? a.chunk : a.hdr[0];
   const int32_t first = a.dir[((int64_t)r * a.qtiles + qt) * a.hkv + g];
-  if (first < 0 || first + ns > units) return;
-  int32_t c0, c1, b0, b1;
-  request_rows(a.cu_ctx, a.cu_blk, r, a.total_ctx, a.total_blk, &c0, &c1, &b0, &b1);
+  const LaneReq q = lane_req(a, r);
+  if (chunk < KT) return;
+  const int32_t ns = req_splits(q, chunk), blen = q.blen, b0 = q.b0;
+  if (ns <= 1 || qt >= q.nq) return;  // unsplit units wrote their output directly
+  if (first < 0 || first + ns > a.units) return;
   const int32_t nrows = a.group * blen;
   const int tid = threadIdx.x;
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
@@ -669,25 +860,18 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPl
   }
   if (p.split_keys > 0) {
     pl.chunk = p.split_keys;
+    pl.units = (int64_t)pl.qtiles * ((eff + pl.chunk - 1) / pl.chunk + p.num_reqs);
   } else {
-    // Resident workgroup slots (two per compute unit at this kernel's LDS use).
-    // If every (request, query tile, kv-head) can have a few units, size the
-    // units so the whole grid is resident at once (no partial second round);
-    // otherwise cut the keys into units of a few rounds' worth.
-    const int64_t slots = 2LL * (num_cus > 0 ? num_cus : 256);
-    const int64_t base = (int64_t)p.num_reqs * p.num_kv_heads * pl.qtiles;
-    const int64_t work = eff * p.num_kv_heads * pl.qtiles;
-    int64_t c;
-    if (2 * base <= slots)
-      c = (work + (slots - base) - 1) / (slots - base);
-    else
-      c = (work + 4 * slots - 1) / (4 * slots);
-    c = (c + KT - 1) / KT * KT;
-    if (c < 128) c = 128;
-    if (c > (1 << 20)) c = 1 << 20;
-    pl.chunk = (int32_t)c;
+    // The device picks the split size (choose_chunk) so that the units fill
+    // the launched grid. Resident workgroup slots: two per compute unit at
+    // this kernel's LDS use. With few (request, query tile) pairs the grid is
+    // one round of slots; with many, two units per pair or two rounds.
+    pl.chunk = 0;
+    const int64_t slots_per_head = std::max<int64_t>(1, 2LL * (num_cus > 0 ? num_cus : 256) / p.num_kv_heads);
+    const int64_t base = (int64_t)p.num_reqs * pl.qtiles;
+    pl.units = (2 * base <= slots_per_head) ? slots_per_head
+                                            : std::max(2 * base, 2 * slots_per_head);
   }
-  pl.units = (int64_t)pl.qtiles * ((eff + pl.chunk - 1) / pl.chunk + p.num_reqs);
   size_t off = 256;  // reserved header
   pl.off_counters = off;
   off = align_up(off + sizeof(int32_t) * (size_t)p.num_reqs * pl.qtiles * p.num_kv_heads, 256);
@@ -701,6 +885,7 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPl
 }
 
 hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnPlan& plan,
+                                  const dflash_qk_prologue* pro,
                                   const int32_t* cu_ctx, const int32_t* cu_blk, const void* q,
                                   const void* kb, const void* vb, const void* kc, const void* vc,
                                   void* out, void* ws, hipStream_t s) {
@@ -730,6 +915,16 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.total_ctx = p.total_ctx; a.total_blk = p.total_blk;
   a.num_reqs = p.num_reqs; a.hq = p.num_q_heads; a.hkv = p.num_kv_heads;
   a.group = plan.group; a.chunk = plan.chunk; a.qtiles = plan.qtiles;
+  a.units = (int32_t)plan.units;
+  a.hdr = (int32_t*)w;
+  if (pro) {
+    a.qnw = pro->q_norm_w;
+    a.knw = pro->k_norm_w;
+    a.bpos = pro->positions;
+    a.rope = reinterpret_cast<const float2*>(pro->rope_table);
+    a.max_pos = pro->max_pos;
+    a.eps = pro->eps;
+  }
   a.max_blk = p.max_blk_len;
   a.scale_log2 = p.scale * LOG2E;
   a.causal = p.causal ? 1 : 0; a.window = p.window;
@@ -741,20 +936,25 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   int dev = 0;
   (void)hipGetDevice(&dev);
   std::call_once(once[dev & 63], [] {
-    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2);
-    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64>,
-                        hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2);
+    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2);
+    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2);
+    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64, false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2);
+    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64, true>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2);
   });
   const int64_t mblocks = (int64_t)p.num_reqs * plan.qtiles * p.num_kv_heads * (QROWS / MROWS);
+  const dim3 grid((unsigned)blocks), blk(NT), mgrid((unsigned)mblocks);
   if (p.head_dim == 128) {
-    hipLaunchKernelGGL(block_attn_bf16_kernel<128>, dim3((unsigned)blocks), dim3(NT), lds, s, a);
-    hipLaunchKernelGGL(block_attn_merge_kernel<128>, dim3((unsigned)mblocks), dim3(NT), 0, s, a,
-                       (int32_t)plan.units);
+    if (pro) hipLaunchKernelGGL((block_attn_bf16_kernel<128, true>), grid, blk, lds, s, a);
+    else hipLaunchKernelGGL((block_attn_bf16_kernel<128, false>), grid, blk, lds, s, a);
+    hipLaunchKernelGGL(block_attn_merge_kernel<128>, mgrid, blk, 0, s, a);
   } else {
-    hipLaunchKernelGGL(block_attn_bf16_kernel<64>, dim3((unsigned)blocks), dim3(NT), lds, s, a);
-    hipLaunchKernelGGL(block_attn_merge_kernel<64>, dim3((unsigned)mblocks), dim3(NT), 0, s, a,
-                       (int32_t)plan.units);
+    if (pro) hipLaunchKernelGGL((block_attn_bf16_kernel<64, true>), grid, blk, lds, s, a);
+    else hipLaunchKernelGGL((block_attn_bf16_kernel<64, false>), grid, blk, lds, s, a);
+    hipLaunchKernelGGL(block_attn_merge_kernel<64>, mgrid, blk, 0, s, a);
   }
   return hipGetLastError();
 }

@@ -139,7 +139,8 @@ size_t dflash_block_attention_workspace_size(const dflash_block_attn_params* p) 
   return plan.bytes;
 }
 
-dflash_status dflash_block_attention(const dflash_block_attn_params* p, const int32_t* cu_ctx_lens,
+dflash_status dflash_block_attention(const dflash_block_attn_params* p,
+                                     const dflash_qk_prologue* prologue, const int32_t* cu_ctx_lens,
                                      const int32_t* cu_blk_lens, const void* q, const void* k_blk,
                                      const void* v_blk, const void* k_ctx, const void* v_ctx,
                                      void* out, void* workspace, size_t workspace_bytes,
@@ -169,9 +170,26 @@ dflash_status dflash_block_attention(const dflash_block_attn_params* p, const in
       return fail(DFLASH_ERR_WORKSPACE, "block_attention: workspace has %zu bytes, %zu needed",
                   workspace_bytes, plan.bytes);
   }
+  if (prologue) {
+    if (p->dtype != DFLASH_BF16)
+      return fail(DFLASH_ERR_UNSUPPORTED, "block_attention: the fused prologue needs bf16");
+    if (p->max_blk_len > 64)
+      return fail(DFLASH_ERR_UNSUPPORTED,
+                  "block_attention: the fused prologue needs max_blk_len <= 64 (got %d)",
+                  p->max_blk_len);
+    if (!prologue->q_norm_w || !prologue->k_norm_w || !prologue->positions || !prologue->rope_table)
+      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: NULL pointer in the prologue");
+    if (!aligned(prologue->q_norm_w, 16) || !aligned(prologue->k_norm_w, 16) ||
+        !aligned(prologue->rope_table, 16))
+      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: prologue tensors must be 16-byte aligned");
+    if (prologue->max_pos < 1)
+      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: prologue max_pos must be >= 1");
+    if (!(prologue->eps >= 0.f) || !std::isfinite(prologue->eps))
+      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: prologue eps must be finite and >= 0");
+  }
   if (plan.units * p->num_kv_heads > INT32_MAX)
     return fail(DFLASH_ERR_UNSUPPORTED, "block_attention: too many work units");
-  return hip_status(dflash::launch_block_attention(*p, plan, cu_ctx_lens, cu_blk_lens, q, k_blk,
+  return hip_status(dflash::launch_block_attention(*p, plan, prologue, cu_ctx_lens, cu_blk_lens, q, k_blk,
                                                    v_blk, k_ctx, v_ctx, out, workspace,
                                                    (hipStream_t)stream),
                     "block_attention launch");

@@ -27,7 +27,7 @@ struct AttnPlan {
 bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPlan* plan);
 
 hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnPlan& plan,
-                                  const int32_t* cu_ctx, const int32_t* cu_blk, const void* q,
+                                  const dflash_qk_prologue* pro, const int32_t* cu_ctx, const int32_t* cu_blk, const void* q,
                                   const void* kb, const void* vb, const void* kc, const void* vc,
                                   void* out, void* ws, hipStream_t s);
 

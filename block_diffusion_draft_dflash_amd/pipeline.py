@@ -84,6 +84,11 @@ class DevicePath:
             self.k_ctx = self.k_ctx_raw.clone()
             self.v_ctx = to_device(wl.v_ctx, dt, device)
         self.out = torch.zeros_like(self.q)
+        # raw copies for the fused path (never modified)
+        self.q_raw = self.q.clone()
+        self.k_blk_raw = self.k_blk.clone()
+        self.prologue = B.make_qk_prologue(self.q_norm_w, self.k_norm_w, self.blk_pos, self.rope,
+                                           wl.eps)
         self.params = B.make_block_attn_params(
             wl.num_reqs, wl.hq, wl.hkv, wl.dh, self.dtype_code, tc, wl.total_blk,
             int(wl.blk_lens.max()) if wl.num_reqs else 0, wl.scale, wl.causal, wl.window,
@@ -115,7 +120,19 @@ class DevicePath:
                                  self.v_blk, self.k_ctx if self.wl.total_ctx else None,
                                  self.v_ctx if self.wl.total_ctx else None, self.out, self.ws)
 
+    def attention_fused(self) -> None:
+        """Block attention with the q/k norm + RoPE fused in (raw q and k_blk)."""
+        B.dflash_block_attention(self.params, self.cu_ctx, self.cu_blk, self.q_raw, self.k_blk_raw,
+                                 self.v_blk, self.k_ctx if self.wl.total_ctx else None,
+                                 self.v_ctx if self.wl.total_ctx else None, self.out, self.ws,
+                                 prologue=self.prologue)
+
     def step(self) -> None:
-        """One pass of the hot path over the batch: q/k norm + RoPE, block attention."""
+        """One pass of the hot path over the batch: q/k norm + RoPE, block attention
+        (two calls; q and k_blk are normalised in place)."""
         self.qk_norm_rope()
         self.attention()
+
+    def step_fused(self) -> None:
+        """One pass of the hot path as a single fused call (bf16)."""
+        self.attention_fused()

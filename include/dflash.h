@@ -121,6 +121,26 @@ typedef struct {
                            else a positive multiple of 64 */
 } dflash_block_attn_params;
 
+/*
+ * Optional fused prologue of dflash_block_attention: when given, q and k_blk
+ * are the RAW projections and the attention applies, on the fly, exactly
+ * what dflash_qk_norm_rope would (per-head RMSNorm with q_norm_w / k_norm_w,
+ * then NeoX RoPE at `positions`), without writing q or k_blk back
+ * ("qwen3_dflash.cpp" page, ForwardBlockLogits: q_norm, k_norm, RopeNeox right
+ * before the block attention; "qwen3.cpp" page header names this fusion
+ * kAttnQkNormRope). Requires dtype == DFLASH_BF16 and max_blk_len <= 64
+ * (DFLASH_ERR_UNSUPPORTED otherwise).
+ */
+typedef struct {
+  const float* q_norm_w;    /* device f32 [Dh] */
+  const float* k_norm_w;    /* device f32 [Dh] */
+  const int32_t* positions; /* device int32 [total_blk]: positions of the block rows,
+                               clamped into [0, max_pos) */
+  const float* rope_table;  /* device f32 [max_pos][Dh/2][2] from dflash_rope_table */
+  int32_t max_pos;
+  float eps;
+} dflash_qk_prologue;
+
 /* Bytes of workspace dflash_block_attention needs for these parameters
  * (0 if they are invalid; see dflash_block_attention_check). */
 size_t dflash_block_attention_workspace_size(const dflash_block_attn_params* p);
@@ -143,8 +163,10 @@ dflash_status dflash_block_attention_check(const dflash_block_attn_params* p);
  * directly).
  *
  *   cu_ctx_lens, cu_blk_lens  device int32 [R+1], nondecreasing, [0] = 0.
- *   q       [total_blk, Hq, Dh]  (already q-normed and rotated)
- *   k_blk   [total_blk, Hkv, Dh] (already k-normed and rotated), v_blk alike.
+ *   prologue  NULL, or the fused q/k norm + RoPE (see dflash_qk_prologue).
+ *   q       [total_blk, Hq, Dh]  (already q-normed and rotated unless prologue)
+ *   k_blk   [total_blk, Hkv, Dh] (already k-normed and rotated unless prologue),
+ *           v_blk alike (raw).
  *   k_ctx   [total_ctx, Hkv, Dh], v_ctx alike; may be NULL if total_ctx == 0.
  *   out     [total_blk, Hq, Dh], written (rows of empty requests untouched).
  *   workspace  device, 256-byte aligned, >= dflash_block_attention_workspace_size
@@ -155,7 +177,9 @@ dflash_status dflash_block_attention_check(const dflash_block_attn_params* p);
  * than through f32 rounding; for a fixed split_keys it is bitwise
  * deterministic.
  */
-dflash_status dflash_block_attention(const dflash_block_attn_params* p, const int32_t* cu_ctx_lens,
+dflash_status dflash_block_attention(const dflash_block_attn_params* p,
+                                     const dflash_qk_prologue* prologue /* NULL: q, k_blk normed */,
+                                     const int32_t* cu_ctx_lens,
                                      const int32_t* cu_blk_lens, const void* q, const void* k_blk,
                                      const void* v_blk, const void* k_ctx, const void* v_ctx,
                                      void* out, void* workspace, size_t workspace_bytes,

@@ -88,11 +88,15 @@ def assert_rounded(wl, got, ref, tag):
     assert not bad.any(), f"{tag}: {bad.sum()} elements beyond one-rounding bound"
 
 
-def run_and_check(wl, split_keys=0, reqs=None, check_intermediates=True, tag=""):
+def run_and_check(wl, split_keys=0, reqs=None, check_intermediates=True, tag="", fused=False):
     torch.cuda.synchronize()
     dp = DevicePath(wl, split_keys=split_keys)
     dp.prepare_context()
-    dp.step()
+    if fused:
+        dp.step_fused()
+        check_intermediates = False
+    else:
+        dp.step()
     torch.cuda.synchronize()
     reqs = list(range(wl.num_reqs)) if reqs is None else reqs
     ref = oracle_outputs(wl, reqs)
@@ -181,3 +185,57 @@ def test_parity_full_swa_sampled():
     print("case full swa", flush=True)
     wl = make_workload("swa")
     run_and_check(wl, reqs=[0, 7, 15], tag="full swa sampled")
+
+
+# ---------------------------------------------------------------- fused q/k norm + RoPE prologue
+
+FUSED = {
+    "qwen3_8b_draft_small": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=100, ctx_hi=700),
+    "large_decode_small": dict(name="large_decode", num_reqs=70, ctx_lo=1, ctx_hi=300),
+    "swa_small": dict(name="swa", num_reqs=3, ctx_len=700, window=256),
+    "empty_ctx_and_blocks": dict(name="qwen3_8b_draft", ctx_lens=[0, 5, 130, 0, 77],
+                                 blk_lens=[3, 0, 17, 40, 1]),
+    "block_64": dict(name="swa", ctx_lens=[40, 301], blk_lens=[64, 33], window=50),
+    "dh64": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=50, ctx_hi=300, hq=8, hkv=2, dh=64),
+    "gqa8": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=200, hq=64, hkv=8),
+}
+
+
+@pytest.mark.parametrize("case", list(FUSED))
+def test_parity_fused_prologue(case):
+    print(f"case fused {case}", flush=True)
+    kw = dict(FUSED[case])
+    name = kw.pop("name")
+    wl = make_workload(name, **kw)
+    run_and_check(wl, tag=f"fused {case}", fused=True)
+
+
+@pytest.mark.parametrize("split", [64, 128])
+def test_parity_fused_forced_splits(split):
+    # splits that cut through the block rows
+    print(f"case fused split {split}", flush=True)
+    wl = make_workload("qwen3_8b_draft", num_reqs=3, ctx_lo=100, ctx_hi=700)
+    run_and_check(wl, split_keys=split, tag=f"fused split {split}", fused=True)
+
+
+def test_parity_fused_full_qwen3_8b_draft():
+    print("case fused full qwen3_8b_draft", flush=True)
+    wl = make_workload("qwen3_8b_draft")
+    run_and_check(wl, tag="fused full qwen3_8b_draft", fused=True)
+
+
+def test_parity_fused_full_ctx_kv_sampled():
+    # the config with hidden states: context K/V from dflash_context_kv, one
+    # request through the oracle's full projection
+    print("case fused full ctx_kv", flush=True)
+    wl = make_workload("ctx_kv")
+    run_and_check(wl, reqs=[2], tag="fused full ctx_kv sampled", fused=True)
+
+
+def test_fused_rejections(dflash):
+    wl = make_workload("tiny")
+    dp = DevicePath(wl)
+    dp.prepare_context()
+    with pytest.raises(dflash.DflashError) as e:
+        dp.attention_fused()  # f32 has no fused prologue
+    assert e.value.status == dflash.DFLASH_ERR_UNSUPPORTED
