@@ -112,6 +112,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="q/k norm + RoPE as a separate in-place call before the attention")
+    ap.add_argument("--device-plan", action="store_true",
+                    help="leave the work split to the kernels (no host copies of the lengths)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB (3 times) so a "
@@ -141,7 +143,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     wl = make_workload(args.workload)
-    paths = [DevicePath(wl, split_keys=args.split_keys) for _ in range(args.rotate)]
+    paths = [DevicePath(wl, split_keys=args.split_keys, host_lengths=not args.device_plan)
+             for _ in range(args.rotate)]
     for p in paths:
         p.prepare_context()
     torch.cuda.synchronize()
@@ -249,6 +252,7 @@ def main() -> int:
             "rotating_copies": len(paths),
             "hip_graph": use_graph,
             "fused_qk_norm_rope": fused,
+            "work_split": "device-planned" if args.device_plan else "host-planned",
         },
         "draft_query_tokens_per_s": tokens_per_s,
         "roofline": {

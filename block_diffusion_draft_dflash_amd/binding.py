@@ -60,6 +60,8 @@ class BlockAttnParams(ctypes.Structure):
         ("causal", ctypes.c_int32),
         ("window", ctypes.c_int32),
         ("split_keys", ctypes.c_int32),
+        ("host_cu_ctx_lens", ctypes.c_void_p),
+        ("host_cu_blk_lens", ctypes.c_void_p),
     ]
 
 
@@ -174,9 +176,22 @@ def dflash_qk_norm_rope(q: Optional[torch.Tensor], k: torch.Tensor,
 def make_block_attn_params(num_reqs: int, num_q_heads: int, num_kv_heads: int, head_dim: int,
                            dtype: int, total_ctx: int, total_blk: int, max_blk_len: int,
                            scale: float, causal: bool = False, window: int = 0,
-                           split_keys: int = 0) -> BlockAttnParams:
-    return BlockAttnParams(num_reqs, num_q_heads, num_kv_heads, head_dim, dtype, total_ctx,
-                           total_blk, max_blk_len, scale, int(bool(causal)), window, split_keys)
+                           split_keys: int = 0, host_cu_ctx_lens=None,
+                           host_cu_blk_lens=None) -> BlockAttnParams:
+    """``host_cu_*``: optional host copies of the cumulative lengths (array-likes
+    of R+1 ints); the returned struct keeps int32 copies of them alive."""
+    p = BlockAttnParams(num_reqs, num_q_heads, num_kv_heads, head_dim, dtype, total_ctx,
+                        total_blk, max_blk_len, scale, int(bool(causal)), window, split_keys,
+                        None, None)
+    if host_cu_ctx_lens is not None or host_cu_blk_lens is not None:
+        if host_cu_ctx_lens is None or host_cu_blk_lens is None:
+            raise ValueError("give both host_cu_ctx_lens and host_cu_blk_lens, or neither")
+        keep = tuple((ctypes.c_int32 * len(a))(*[int(x) for x in a])
+                     for a in (host_cu_ctx_lens, host_cu_blk_lens))
+        p._host_lens = keep
+        p.host_cu_ctx_lens = ctypes.cast(keep[0], ctypes.c_void_p)
+        p.host_cu_blk_lens = ctypes.cast(keep[1], ctypes.c_void_p)
+    return p
 
 
 def dflash_block_attention_check(p: BlockAttnParams) -> int:

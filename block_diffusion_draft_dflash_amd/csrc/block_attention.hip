@@ -38,6 +38,21 @@ constexpr int KT = 32;     // keys per tile
 constexpr int NT = 256;    // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Work split planned on the host from host copies of the lengths, passed
+// by value with the launch (kernel arguments): for each request its rows,
+// visible key range, split size, split count and first unit, and for each
+// unit (per kv-head) its request. nreq == 0: plan on the device instead.
+constexpr int HS_MAX_REQS = 64;
+constexpr int HS_MAX_UNITS = 512;
+struct ReqSched {
+  int32_t c0, b0, clen, blen, lo, csz, ns, ubase;
+};
+struct HostSched {
+  int32_t nreq, chunk, nunits, pad;
+  uint8_t unit_req[HS_MAX_UNITS];
+  ReqSched req[HS_MAX_REQS];
+};
+
 struct AttnArgs {
   const int32_t* cu_ctx;
   const int32_t* cu_blk;
@@ -64,6 +79,7 @@ struct AttnArgs {
   float eps;
   float scale_log2;
   int32_t causal, window;
+  HostSched hs;
 };
 
 struct Unit {
@@ -118,6 +134,11 @@ __device__ __forceinline__ int32_t wave_sum(int32_t v) {
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
 }
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
 __device__ __forceinline__ int32_t wave_max(int32_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
@@ -146,21 +167,22 @@ struct ReqView {
 __device__ int32_t choose_chunk(const AttnArgs& a, const ReqView& rv) {
   if (a.chunk > 0) return a.chunk;
   auto count = [&](int32_t c) {
-    int32_t tot = 0;
+    int64_t tot = 0;
     for (int32_t r0 = 0; r0 < a.num_reqs; r0 += 64) {
       const LaneReq q = rv.group(r0);
-      tot += wave_sum(req_splits(q, c) * q.nq);
+      tot += wave_sum64((int64_t)req_splits(q, c) * q.nq);
     }
     return tot;
   };
-  int32_t maxn = 0, work = 0;
+  int32_t maxn = 0;
+  int64_t work = 0;
   for (int32_t r0 = 0; r0 < a.num_reqs; r0 += 64) {
     const LaneReq q = rv.group(r0);
     maxn = max(maxn, wave_max(q.n));
-    work += wave_sum(((q.n + KT - 1) / KT) * q.nq);  // in tiles
+    work += wave_sum64((int64_t)((q.n + KT - 1) / KT) * q.nq);  // in tiles
   }
   const int32_t kmax = max(1, (maxn + KT - 1) / KT);
-  int32_t klo = max(1, min(kmax, (work + a.units - 1) / max(a.units, 1)));
+  int32_t klo = (int32_t)max((int64_t)1, min((int64_t)kmax, (work + a.units - 1) / max(a.units, 1)));
   if (count(klo * KT) <= a.units) return klo * KT;
   // grow geometrically, then bisect: count() is non-increasing in c
   int32_t khi = klo, step = 1;
@@ -321,11 +343,26 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
 
   const int32_t g = blockIdx.x % a.hkv;
   const int32_t u = blockIdx.x / a.hkv;
-  const ReqView rv(a);
-  const int32_t chunk = __builtin_amdgcn_readfirstlane(choose_chunk(a, rv));
-  if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[0] = chunk;  // for the merge kernel
   Unit un;
-  if (!find_unit(a, rv, chunk, u, &un)) return;  // uniform over the workgroup
+  if (a.hs.nreq > 0) {
+    // planned on the host: the unit's request and its numbers are kernel arguments
+    if (u >= a.hs.nunits) return;
+    const int32_t r = a.hs.unit_req[u];
+    const ReqSched& q = a.hs.req[r];
+    const int32_t loc = u - q.ubase;
+    un.r = r;
+    un.qt = loc / q.ns;
+    un.s = loc - un.qt * q.ns;
+    un.nsplit = q.ns;
+    un.first = q.ubase + un.qt * q.ns;
+    un.clen = q.clen; un.blen = q.blen; un.lo = q.lo; un.csz = q.csz;
+    un.ctx0 = q.c0; un.blk0 = q.b0;
+  } else {
+    const ReqView rv(a);
+    const int32_t chunk = __builtin_amdgcn_readfirstlane(choose_chunk(a, rv));
+    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[0] = chunk;  // for the merge kernel
+    if (!find_unit(a, rv, chunk, u, &un)) return;  // uniform over the workgroup
+  }
   // Every lane holds the same unit; say so to the compiler (scalar registers,
   // scalar branches).
   un.r = uni(un.r); un.qt = uni(un.qt); un.s = uni(un.s); un.nsplit = uni(un.nsplit);
@@ -637,7 +674,7 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
       float2* pml = reinterpret_cast<float2*>(a.part_ml) + (int64_t)blockIdx.x * QROWS + nrow_unit;
       *pml = make_float2(mx, ltot);
     }
-    if (un.s == 0 && tid == 0)
+    if (un.s == 0 && tid == 0 && a.hs.nreq == 0)
       a.dir[((int64_t)un.r * a.qtiles + un.qt) * a.hkv + g] = un.first;
   }
 }
@@ -652,7 +689,7 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
   constexpr int DV = 8;                   // head-dim values per thread
   constexpr int TPR = DH / DV;            // threads per row
   constexpr int RPW = NT / TPR;           // rows per workgroup pass
-  constexpr int MB = 4;
+  constexpr int MB = 8;
   const int32_t rb_count = QROWS / MROWS;
   int64_t id = blockIdx.x;
   const int32_t rb = (int32_t)(id % rb_count); id /= rb_count;
@@ -660,15 +697,23 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
   const int32_t qt = (int32_t)(id % a.qtiles); id /= a.qtiles;
   const int32_t r = (int32_t)id;
   if (r >= a.num_reqs) return;
-  // The split size (chosen by the main kernel of this call unless fixed), the
-  // directory entry and the lengths are independent loads.
-  const int32_t chunk = a.chunk > 0 ? a.chunk : a.hdr[0];
-  const int32_t first = a.dir[((int64_t)r * a.qtiles + qt) * a.hkv + g];
-  const LaneReq q = lane_req(a, r);
-  if (chunk < KT) return;
-  const int32_t ns = req_splits(q, chunk), blen = q.blen, b0 = q.b0;
-  if (ns <= 1 || qt >= q.nq) return;  // unsplit units wrote their output directly
-  if (first < 0 || first + ns > a.units) return;
+  int32_t ns, blen, b0, first;
+  if (a.hs.nreq > 0) {
+    const ReqSched& q = a.hs.req[r];
+    ns = q.ns; blen = q.blen; b0 = q.b0;
+    if (ns <= 1 || qt * QROWS >= a.group * blen) return;
+    first = q.ubase + qt * ns;
+  } else {
+    // The split size (chosen by the main kernel of this call unless fixed), the
+    // directory entry and the lengths are independent loads.
+    const int32_t chunk = a.chunk > 0 ? a.chunk : a.hdr[0];
+    first = a.dir[((int64_t)r * a.qtiles + qt) * a.hkv + g];
+    const LaneReq q = lane_req(a, r);
+    if (chunk < KT) return;
+    ns = req_splits(q, chunk); blen = q.blen; b0 = q.b0;
+    if (ns <= 1 || qt >= q.nq) return;  // unsplit units wrote their output directly
+    if (first < 0 || first + ns > a.units) return;
+  }
   const int32_t nrows = a.group * blen;
   const int tid = threadIdx.x;
   const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
@@ -846,6 +891,89 @@ __global__ __launch_bounds__(64) void block_attn_f32_kernel(F32Args a) {
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Host mirror of lane_req / choose_chunk / find_unit's numbering: the same
+// integer arithmetic on the host copies of the lengths, so the plan (and the
+// result) is the one the kernels would derive on the device.
+struct HostReq {
+  int32_t c0, b0, clen, blen, lo, n, nq;
+};
+HostReq host_req(const dflash_block_attn_params& p, int32_t group, int32_t r) {
+  const int32_t* hc = p.host_cu_ctx_lens;
+  const int32_t* hb = p.host_cu_blk_lens;
+  const int32_t tc = (int32_t)p.total_ctx, tb = (int32_t)p.total_blk;
+  HostReq q{};
+  q.c0 = std::min(std::max(hc[r], 0), tc);
+  const int32_t c1 = std::min(std::max(hc[r + 1], q.c0), tc);
+  q.b0 = std::min(std::max(hb[r], 0), tb);
+  const int32_t b1 = std::min(std::max(hb[r + 1], q.b0), tb);
+  q.clen = c1 - q.c0;
+  q.blen = std::min(b1 - q.b0, p.max_blk_len);
+  q.lo = (p.causal && p.window > 0) ? std::max(q.clen - p.window + 1, 0) : 0;
+  q.n = q.blen > 0 ? q.clen + q.blen - q.lo : 0;
+  q.nq = q.blen > 0 ? (group * q.blen + QROWS - 1) / QROWS : 0;
+  return q;
+}
+int32_t host_splits(const HostReq& q, int32_t chunk) {
+  return q.n > 0 ? (q.n + chunk - 1) / chunk : 0;
+}
+int32_t host_split_size(const HostReq& q, int32_t ns) {
+  return ns > 0 ? ((q.n + ns - 1) / ns + KT - 1) / KT * KT : 0;
+}
+int32_t host_choose_chunk(const HostReq* rq, int32_t nreq, int32_t units) {
+  auto count = [&](int32_t c) {
+    int64_t tot = 0;
+    for (int32_t r = 0; r < nreq; ++r) tot += (int64_t)host_splits(rq[r], c) * rq[r].nq;
+    return tot;
+  };
+  int32_t maxn = 0;
+  int64_t work = 0;
+  for (int32_t r = 0; r < nreq; ++r) {
+    maxn = std::max(maxn, rq[r].n);
+    work += (int64_t)((rq[r].n + KT - 1) / KT) * rq[r].nq;
+  }
+  const int32_t kmax = std::max(1, (maxn + KT - 1) / KT);
+  int32_t klo = (int32_t)std::max<int64_t>(
+      1, std::min<int64_t>(kmax, (work + units - 1) / std::max(units, 1)));
+  if (count(klo * KT) <= units) return klo * KT;
+  int32_t khi = klo, step = 1;
+  while (khi < kmax) {
+    khi = std::min(kmax, khi + step);
+    step *= 2;
+    if (count(khi * KT) <= units) break;
+    klo = khi;
+  }
+  while (khi - klo > 1) {
+    const int32_t mid = (klo + khi) / 2;
+    if (count(mid * KT) <= units) khi = mid; else klo = mid;
+  }
+  return khi * KT;
+}
+// Fill hs from the host lengths; false (hs->nreq = 0) when they are absent or
+// the plan does not fit the table.
+bool plan_host_schedule(const dflash_block_attn_params& p, const AttnPlan& plan, HostSched* hs) {
+  hs->nreq = 0;
+  if (!p.host_cu_ctx_lens || !p.host_cu_blk_lens) return false;
+  if (p.num_reqs > HS_MAX_REQS || plan.units > INT32_MAX) return false;
+  HostReq rq[HS_MAX_REQS];
+  for (int32_t r = 0; r < p.num_reqs; ++r) rq[r] = host_req(p, plan.group, r);
+  const int32_t units = (int32_t)plan.units;
+  const int32_t chunk = plan.chunk > 0 ? plan.chunk : host_choose_chunk(rq, p.num_reqs, units);
+  int32_t ubase = 0;
+  for (int32_t r = 0; r < p.num_reqs; ++r) {
+    const int32_t ns = host_splits(rq[r], chunk);
+    const int32_t cnt = ns * rq[r].nq;
+    if (ubase + cnt > HS_MAX_UNITS || ubase + cnt > units) return false;
+    hs->req[r] = ReqSched{rq[r].c0, rq[r].b0, rq[r].clen, rq[r].blen, rq[r].lo,
+                          host_split_size(rq[r], ns), ns, ubase};
+    for (int32_t k = 0; k < cnt; ++k) hs->unit_req[ubase + k] = (uint8_t)r;
+    ubase += cnt;
+  }
+  hs->chunk = chunk;
+  hs->nunits = ubase;
+  hs->nreq = p.num_reqs;
+  return true;
+}
+
 }  // namespace
 
 bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPlan* plan) {
@@ -928,7 +1056,10 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.max_blk = p.max_blk_len;
   a.scale_log2 = p.scale * LOG2E;
   a.causal = p.causal ? 1 : 0; a.window = p.window;
-  const int64_t blocks = plan.units * p.num_kv_heads;
+  plan_host_schedule(p, plan, &a.hs);
+  // Host-planned: launch only the units the plan uses.
+  const int64_t blocks = (a.hs.nreq > 0 ? a.hs.nunits : plan.units) * p.num_kv_heads;
+  if (blocks == 0) return hipSuccess;
   const size_t lds = (size_t)NSTAGE * 2 * KT * p.head_dim * sizeof(bf16);
   // The LDS limit attribute is a per-function setting: raise it once per
   // device (not per launch, so that stream capture sees only the launch).

@@ -61,7 +61,7 @@ extern "C" {
 
 const char* dflash_last_error(void) { return g_last_error.c_str(); }
 
-int dflash_abi_version(void) { return 100; }
+int dflash_abi_version(void) { return 101; }
 
 dflash_status dflash_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
                                 void* stream) {
@@ -129,6 +129,29 @@ dflash_status dflash_block_attention_check(const dflash_block_attn_params* p) {
   if (p->split_keys < 0 || p->split_keys % 64 != 0 || p->split_keys > (1 << 24))
     return fail(DFLASH_ERR_INVALID_ARG,
                 "block_attention: split_keys must be 0 or a positive multiple of 64 up to 2^24");
+  if (!p->host_cu_ctx_lens != !p->host_cu_blk_lens)
+    return fail(DFLASH_ERR_INVALID_ARG,
+                "block_attention: give both host_cu_ctx_lens and host_cu_blk_lens, or neither");
+  if (p->host_cu_ctx_lens) {
+    const int32_t* hc = p->host_cu_ctx_lens;
+    const int32_t* hb = p->host_cu_blk_lens;
+    if (hc[0] != 0 || hb[0] != 0)
+      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: host cu lengths must start at 0");
+    for (int32_t r = 0; r < p->num_reqs; ++r) {
+      if (hc[r + 1] < hc[r] || hb[r + 1] < hb[r])
+        return fail(DFLASH_ERR_INVALID_ARG,
+                    "block_attention: host cu lengths must be nondecreasing (request %d)", r);
+      if (hb[r + 1] - hb[r] > p->max_blk_len)
+        return fail(DFLASH_ERR_INVALID_ARG,
+                    "block_attention: request %d has %d block rows > max_blk_len %d", r,
+                    hb[r + 1] - hb[r], p->max_blk_len);
+    }
+    if (hc[p->num_reqs] != p->total_ctx || hb[p->num_reqs] != p->total_blk)
+      return fail(DFLASH_ERR_INVALID_ARG,
+                  "block_attention: host cu lengths end at %d / %d, expected total_ctx %lld / "
+                  "total_blk %lld", hc[p->num_reqs], hb[p->num_reqs], (long long)p->total_ctx,
+                  (long long)p->total_blk);
+  }
   return ok();
 }
 

@@ -7,7 +7,11 @@ through the C ABI:
 * context rows: ``dflash_context_kv`` from hidden states when the workload has
   them, else the K-only ``dflash_qk_norm_rope`` on the raw context keys;
 * the step: ``dflash_qk_norm_rope`` on the block's q and k (in place), then
-  ``dflash_block_attention`` over [context; block].
+  ``dflash_block_attention`` over [context; block]; or the one fused call.
+
+By default the host copies of the cumulative lengths go with the attention
+parameters (the work split is then planned on the host); ``host_lengths=False``
+leaves the planning to the kernels.
 
 Only argument marshalling happens here; every step runs in the HIP library.
 """
@@ -40,7 +44,7 @@ def to_host_f64(t: torch.Tensor) -> np.ndarray:
 
 class DevicePath:
     def __init__(self, wl: Workload, device: str = "cuda", split_keys: int = 0,
-                 max_pos: Optional[int] = None):
+                 max_pos: Optional[int] = None, host_lengths: bool = True):
         self.wl = wl
         self.device = device
         dt = wl.dtype
@@ -92,7 +96,9 @@ class DevicePath:
         self.params = B.make_block_attn_params(
             wl.num_reqs, wl.hq, wl.hkv, wl.dh, self.dtype_code, tc, wl.total_blk,
             int(wl.blk_lens.max()) if wl.num_reqs else 0, wl.scale, wl.causal, wl.window,
-            split_keys)
+            split_keys,
+            host_cu_ctx_lens=wl.cu_ctx if host_lengths else None,
+            host_cu_blk_lens=wl.cu_blk if host_lengths else None)
         self.ws = B.alloc_workspace(B.dflash_block_attention_workspace_size(self.params), device)
 
     # ---------------------------------------------------------------- context

@@ -119,6 +119,19 @@ typedef struct {
   int32_t window;       /* 0: none; > 0 (causal only): keys with i - k < window */
   int32_t split_keys;   /* keys per work unit; 0 = chosen by the library,
                            else a positive multiple of 64 */
+  /* Optional HOST copies of cu_ctx_lens / cu_blk_lens (int32 [R+1] each, equal
+   * to the device arrays; both or neither). With them the split of the keys
+   * into work units is planned on the host and handed to the kernels with the
+   * launch (up to 64 requests and 512 units per kv-head; beyond that, and when
+   * NULL, the kernels plan it from the device arrays; the result is the same
+   * either way). They are read during the call only; under stream capture the
+   * plan is fixed into the graph, so the lengths must not change between
+   * replays. Checked: [0] = 0, nondecreasing, cu_ctx_lens[R] = total_ctx,
+   * cu_blk_lens[R] = total_blk, block lengths <= max_blk_len. The pages build
+   * the same per-request offsets on the host ("qwen3_dflash.cpp" page,
+   * ForwardWithCtxKVDev: cu_comb and the index maps from host vectors). */
+  const int32_t* host_cu_ctx_lens;
+  const int32_t* host_cu_blk_lens;
 } dflash_block_attn_params;
 
 /*

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_error_string(lib):
-    assert lib.dflash_abi_version() == 100
+    assert lib.dflash_abi_version() == 101
     assert isinstance(lib.dflash_last_error(), bytes)
 
 
@@ -97,6 +97,41 @@ def test_block_attention_validation(lib, kw, status):
     if status != B.DFLASH_OK:
         assert B.dflash_last_error()
         assert B.dflash_block_attention_workspace_size(p) == 0
+
+
+def _host_lens(ctx, blk):
+    return dict(host_cu_ctx_lens=[0] + list(__import__("itertools").accumulate(ctx)),
+                host_cu_blk_lens=[0] + list(__import__("itertools").accumulate(blk)))
+
+
+@pytest.mark.parametrize("ctx,blk,over,status", [
+    ([1000] * 8 + [0] * 0, [16] * 8, {}, B.DFLASH_OK),
+    ([2000] * 5, [16] * 5, dict(num_reqs=4), B.DFLASH_ERR_INVALID_ARG),      # [R] != totals
+    ([1250] * 8, [16] * 7 + [17], dict(total_blk=129), B.DFLASH_ERR_INVALID_ARG),  # > max_blk_len
+    ([1250] * 8, [16] * 8, dict(total_ctx=10001), B.DFLASH_ERR_INVALID_ARG),  # ctx end mismatch
+])
+def test_host_lengths_validation(lib, ctx, blk, over, status):
+    kw = dict(total_ctx=sum(ctx), total_blk=sum(blk), num_reqs=len(ctx))
+    kw.update(over)
+    kw.update(_host_lens(ctx, blk))
+    p = P(**kw)
+    assert B.dflash_block_attention_check(p) == status, B.dflash_last_error()
+
+
+def test_host_lengths_shape_errors(lib):
+    good = _host_lens([1250] * 8, [16] * 8)
+    p = P(**good)
+    assert B.dflash_block_attention_check(p) == B.DFLASH_OK
+    # a decreasing step, a nonzero start, only one of the two arrays
+    bad = dict(good, host_cu_ctx_lens=[0, 2000, 1000] + good["host_cu_ctx_lens"][3:])
+    assert B.dflash_block_attention_check(P(**bad)) == B.DFLASH_ERR_INVALID_ARG
+    bad = dict(good, host_cu_blk_lens=[1] + good["host_cu_blk_lens"][1:])
+    assert B.dflash_block_attention_check(P(**bad)) == B.DFLASH_ERR_INVALID_ARG
+    with pytest.raises(ValueError):
+        P(host_cu_ctx_lens=good["host_cu_ctx_lens"])
+    q = P()
+    q.host_cu_ctx_lens = ctypes.cast(p._host_lens[0], ctypes.c_void_p)
+    assert B.dflash_block_attention_check(q) == B.DFLASH_ERR_INVALID_ARG
 
 
 def test_workspace_sizes(lib):

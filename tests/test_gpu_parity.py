@@ -88,9 +88,10 @@ def assert_rounded(wl, got, ref, tag):
     assert not bad.any(), f"{tag}: {bad.sum()} elements beyond one-rounding bound"
 
 
-def run_and_check(wl, split_keys=0, reqs=None, check_intermediates=True, tag="", fused=False):
+def run_and_check(wl, split_keys=0, reqs=None, check_intermediates=True, tag="", fused=False,
+                  host_lengths=True):
     torch.cuda.synchronize()
-    dp = DevicePath(wl, split_keys=split_keys)
+    dp = DevicePath(wl, split_keys=split_keys, host_lengths=host_lengths)
     dp.prepare_context()
     if fused:
         dp.step_fused()
@@ -163,6 +164,24 @@ def test_parity_edges(case):
     name = kw.pop("name")
     wl = make_workload(name, **kw)
     run_and_check(wl, tag=f"edge {case}")
+
+
+@pytest.mark.parametrize("case", ["empty_ctx_and_blocks", "dh64_bf16", "causal_long_block",
+                                  "window1"])
+def test_parity_edges_device_planned(case):
+    # the work split derived by the kernels from the device lengths alone
+    print(f"case edge device-planned {case}", flush=True)
+    kw = dict(EDGE[case])
+    name = kw.pop("name")
+    wl = make_workload(name, **kw)
+    run_and_check(wl, tag=f"edge device-planned {case}", host_lengths=False)
+
+
+def test_parity_many_requests_device_planned():
+    # more requests than the host table holds: planned on the device either way
+    print("case 70 requests", flush=True)
+    wl = make_workload("large_decode", num_reqs=70, ctx_lo=1, ctx_hi=300)
+    run_and_check(wl, tag="70 requests", fused=True)
 
 
 # ---------------------------------------------------------------- full sizes (sampled)
