@@ -40,8 +40,12 @@ constexpr float LOG2E = 1.4426950408889634f;
 
 // Work split planned on the host from host copies of the lengths, passed
 // by value with the launch (kernel arguments): for each request its rows,
-// visible key range, split size, split count and first unit, and for each
-// unit (per kv-head) its request. nreq == 0: plan on the device instead.
+// visible key range, split size, split count and first unit, and the launch
+// order of the units (per kv-head) as (request, index within the request's
+// units), largest units first so that the dispatcher's in-order list
+// scheduling balances unequal units. A unit's partial slot is its canonical
+// (request-major) index, whatever its launch position. nreq == 0: plan on the
+// device instead.
 constexpr int HS_MAX_REQS = 64;
 constexpr int HS_MAX_UNITS = 512;
 struct ReqSched {
@@ -49,7 +53,7 @@ struct ReqSched {
 };
 struct HostSched {
   int32_t nreq, chunk, nunits, pad;
-  uint8_t unit_req[HS_MAX_UNITS];
+  uint16_t order[HS_MAX_UNITS];  // launch position -> (request << 8) | unit index in request
   ReqSched req[HS_MAX_REQS];
 };
 
@@ -342,14 +346,16 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][K | V][KT][DH]
 
   const int32_t g = blockIdx.x % a.hkv;
-  const int32_t u = blockIdx.x / a.hkv;
+  int32_t u = blockIdx.x / a.hkv;  // canonical unit index (partial slot)
   Unit un;
   if (a.hs.nreq > 0) {
     // planned on the host: the unit's request and its numbers are kernel arguments
     if (u >= a.hs.nunits) return;
-    const int32_t r = a.hs.unit_req[u];
+    const int32_t e = a.hs.order[u];
+    const int32_t r = e >> 8;
+    const int32_t loc = e & 255;
     const ReqSched& q = a.hs.req[r];
-    const int32_t loc = u - q.ubase;
+    u = q.ubase + loc;
     un.r = r;
     un.qt = loc / q.ns;
     un.s = loc - un.qt * q.ns;
@@ -666,12 +672,13 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
   // Split: publish the partial (unnormalised O, reference max, sum). The
   // merge kernel that follows on the stream combines the splits.
   {
-    float* po = a.part_o + ((int64_t)blockIdx.x * QROWS + nrow_unit) * DH + 4 * j;
+    const int64_t slot = (int64_t)u * a.hkv + g;
+    float* po = a.part_o + (slot * QROWS + nrow_unit) * DH + 4 * j;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       *reinterpret_cast<f32x4*>(po + 16 * dt) = acc_o[dt];
     if (j == 0) {
-      float2* pml = reinterpret_cast<float2*>(a.part_ml) + (int64_t)blockIdx.x * QROWS + nrow_unit;
+      float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot * QROWS + nrow_unit;
       *pml = make_float2(mx, ltot);
     }
     if (un.s == 0 && tid == 0 && a.hs.nreq == 0)
@@ -959,15 +966,25 @@ bool plan_host_schedule(const dflash_block_attn_params& p, const AttnPlan& plan,
   const int32_t units = (int32_t)plan.units;
   const int32_t chunk = plan.chunk > 0 ? plan.chunk : host_choose_chunk(rq, p.num_reqs, units);
   int32_t ubase = 0;
+  // (keys, canonical index, entry) of every unit; sorted by decreasing keys
+  std::pair<int32_t, int32_t> key[HS_MAX_UNITS];
+  uint16_t ent[HS_MAX_UNITS];
   for (int32_t r = 0; r < p.num_reqs; ++r) {
     const int32_t ns = host_splits(rq[r], chunk);
     const int32_t cnt = ns * rq[r].nq;
-    if (ubase + cnt > HS_MAX_UNITS || ubase + cnt > units) return false;
-    hs->req[r] = ReqSched{rq[r].c0, rq[r].b0, rq[r].clen, rq[r].blen, rq[r].lo,
-                          host_split_size(rq[r], ns), ns, ubase};
-    for (int32_t k = 0; k < cnt; ++k) hs->unit_req[ubase + k] = (uint8_t)r;
+    if (cnt > 256 || ubase + cnt > HS_MAX_UNITS || ubase + cnt > units) return false;
+    const int32_t csz = host_split_size(rq[r], ns);
+    hs->req[r] = ReqSched{rq[r].c0, rq[r].b0, rq[r].clen, rq[r].blen, rq[r].lo, csz, ns, ubase};
+    for (int32_t k = 0; k < cnt; ++k) {
+      const int32_t s = k % ns;
+      const int32_t keys = std::min(csz, rq[r].n - s * csz);
+      key[ubase + k] = {-keys, ubase + k};
+      ent[ubase + k] = (uint16_t)((r << 8) | k);
+    }
     ubase += cnt;
   }
+  std::sort(key, key + ubase);
+  for (int32_t i = 0; i < ubase; ++i) hs->order[i] = ent[key[i].second];
   hs->chunk = chunk;
   hs->nunits = ubase;
   hs->nreq = p.num_reqs;
