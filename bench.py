@@ -214,6 +214,29 @@ def main() -> int:
     achieved_gbs = bytes_attn / (attn_us * 1e-6) / 1e9
     traffic = committed_traffic(args.workload)
 
+    # Context-K/V precompute (hidden-state workloads): the dflash_context_kv
+    # call (weight fold, row rms, fused GEMM + k-norm + RoPE), HIP events on
+    # its stream, against the dense bf16 MFMA peak.
+    ckv = None
+    if wl.hidden is not None:
+        p0 = paths[0]
+        p0.prepare_context()
+        torch.cuda.synchronize()
+        reps = 5
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            p0.prepare_context()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ckv_ms = e0.elapsed_time(e1) / reps
+        ckv_flops = 2.0 * wl.total_ctx * wl.hidden_size * (2 * wl.hkv * wl.dh)
+        ckv = {"ms": ckv_ms, "tflops": ckv_flops / (ckv_ms * 1e-3) / 1e12,
+               "peak_tflops": BF16_PEAK_TFLOPS,
+               "frac": ckv_flops / (ckv_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+               "flops": ckv_flops, "rows": wl.total_ctx, "hidden": wl.hidden_size}
+
     cpu = None
     if args.cpu_budget > 0:
         t_cpu, reps, threads = cpu_baseline(wl, args.cpu_budget)
@@ -268,6 +291,7 @@ def main() -> int:
             "avg_launch_us": attn_us,
         },
         "cpu_baseline": cpu,
+        "context_kv": ckv,
         "algorithmic": {"attention_bytes": bytes_attn, "attention_flops": flops_attn,
                         "prologue_bytes": bytes_pro},
     }

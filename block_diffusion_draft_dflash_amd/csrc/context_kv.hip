@@ -13,7 +13,11 @@
 // applied in the GEMM epilogue. The GEMM (M = rows, N = 2 * Hkv * Dh, K = H)
 // runs on v_mfma_f32_16x16x32_bf16 with 256x256 workgroup tiles; each wave owns
 // 128 rows x one 128-wide head, so the k-norm and the rotate-half pairs
-// (d, d + 64) are resolved in registers of one wave.
+// (d, d + 64) are resolved in registers of one wave. The k-slices of A and B
+// are copied HBM -> LDS directly (no register staging), NSTAGE - 1 slices
+// ahead, with explicit waits and fence-free barriers.
+#include <mutex>
+
 #include "dflash_device.h"
 #include "dflash_internal.h"
 
@@ -85,44 +89,76 @@ struct CkvArgs {
 // at one logical chunk touch distinct banks.
 __device__ __forceinline__ int tswz(int row, int c) { return c ^ ((row >> 2) & 3); }
 
+constexpr int NSTAGE = 4;  // LDS stages of (A, B) k-slices: NSTAGE - 1 in flight
+
+// s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
+// 3:0 and 15:14; expcnt and lgkmcnt left at their no-wait maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// Workgroup barrier without the memory fence of __syncthreads() (which would
+// drain the k-slices still in flight).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __global__ __launch_bounds__(NT) void ctx_kv_gemm_kernel(CkvArgs a) {
   constexpr int DH = 128;
   constexpr int HALF = DH / 2;
-  constexpr int TILE = BM * BK;  // elements per A (or B) tile
-  constexpr int LOADS = TILE / 8 / NT;  // 16-byte loads per thread per tile (4)
+  constexpr int TILE = BM * BK;         // elements per A (or B) k-slice
+  constexpr int CPW = TILE / 512 / 4;   // 1 KB copies per wave per operand per k-slice (4)
+  constexpr int CPS = 2 * CPW;          // per thread per k-slice (A and B)
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][A | B]
 
+  // Block order: the dispatcher deals workgroups to the 8 XCDs round-robin.
+  // Consecutive row blocks go to different XCDs and each XCD runs all column
+  // tiles of its row blocks, so an XCD's L2 fetches each A row block once
+  // (B, 16 MB at most, is shared through the last-level cache).
   const int ntn = a.n / BN;
-  const int nt_idx = blockIdx.x % ntn;
-  const int64_t row0 = (int64_t)(blockIdx.x / ntn) * BM;
-  const int col0 = nt_idx * BN;
+  const int xcd = blockIdx.x % 8;
+  const int slot = blockIdx.x / 8;
+  const int64_t rb = (int64_t)(slot / ntn) * 8 + xcd;
+  const int64_t row0 = rb * BM;
+  if (row0 >= a.rows) return;
+  const int col0 = (slot % ntn) * BN;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, m = lane & 15, j = lane >> 4;
   const int wm = w >> 1, wn = w & 1;
 
-  bf16x8 areg[LOADS], breg[LOADS];
-  auto load = [&](int32_t k0) {
+  // Copies: one wave-wide 16-byte-per-lane load fills 1 KB = 16 tile rows of
+  // LDS in lane order; lane L takes the logical chunk the swizzle stores at
+  // its slot. Rows past the end re-read the last row (their results are not
+  // stored).
+  const bf16* asrc[CPW];
+  const bf16* bsrc[CPW];
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int id = tid + NT * it;
-      const int r = id >> 2, c = id & 3;
-      const int64_t grow = row0 + r;
-      areg[it] = grow < a.rows
-                     ? *reinterpret_cast<const bf16x8*>(a.h + grow * a.hidden + k0 + c * 8)
-                     : bf16x8{};
-      breg[it] = *reinterpret_cast<const bf16x8*>(a.w + (int64_t)(col0 + r) * a.hidden + k0 + c * 8);
-    }
+  for (int i = 0; i < CPW; ++i) {
+    const int r = (w * CPW + i) * 16 + lane / 4;
+    const int c = tswz(r, lane % 4);
+    const int64_t grow = min(row0 + r, a.rows - 1);
+    asrc[i] = a.h + grow * a.hidden + c * 8;
+    bsrc[i] = a.w + (int64_t)(col0 + r) * a.hidden + c * 8;
+  }
+  auto dma = [](const bf16* src, bf16* dst) {
+    const uint32_t lds_addr =
+        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)dst);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(lds_addr), "v"(src)
+                 : "memory", "m0");
   };
-  auto store = [&](int st) {
-    bf16* as = smem + st * 2 * TILE;
+  auto issue = [&](int32_t ks) {
+    bf16* as = smem + (ks % NSTAGE) * 2 * TILE;
     bf16* bs = as + TILE;
+    const int32_t k0 = ks * BK;
 #pragma unroll
-    for (int it = 0; it < LOADS; ++it) {
-      const int id = tid + NT * it;
-      const int r = id >> 2, c = id & 3;
-      const int off = r * BK + tswz(r, c) * 8;
-      *reinterpret_cast<bf16x8*>(as + off) = areg[it];
-      *reinterpret_cast<bf16x8*>(bs + off) = breg[it];
+    for (int i = 0; i < CPW; ++i) {
+      dma(asrc[i] + k0, as + (w * CPW + i) * 512);
+      dma(bsrc[i] + k0, bs + (w * CPW + i) * 512);
     }
   };
 
@@ -133,30 +169,33 @@ __global__ __launch_bounds__(NT) void ctx_kv_gemm_kernel(CkvArgs a) {
     for (int y = 0; y < 8; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int32_t ksteps = a.hidden / BK;
-  load(0);
-  store(0);
-  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < NSTAGE - 1; ++t)
+    if (t < ksteps) issue(t);
   for (int32_t ks = 0; ks < ksteps; ++ks) {
-    const int st = ks & 1;
-    const bool has_next = ks + 1 < ksteps;
-    if (has_next) load((ks + 1) * BK);
-    const bf16* as = smem + st * 2 * TILE;
+    // own copies of slice ks landed (later slices may stay in flight); the
+    // barrier publishes every wave's part and frees the stage of slice ks-1
+    const int32_t after = min(ksteps - 1 - ks, NSTAGE - 2);
+    if (after >= 2) wait_vmcnt<2 * CPS>();
+    else if (after == 1) wait_vmcnt<CPS>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (ks + NSTAGE - 1 < ksteps) issue(ks + NSTAGE - 1);
+    const bf16* as = smem + (ks % NSTAGE) * 2 * TILE;
     const bf16* bs = as + TILE;
     bf16x8 af[8], bfr[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int ra = 128 * wm + 16 * x + m;
       af[x] = *reinterpret_cast<const bf16x8*>(as + ra * BK + tswz(ra, j) * 8);
-      const int rb = 128 * wn + 16 * x + m;
-      bfr[x] = *reinterpret_cast<const bf16x8*>(bs + rb * BK + tswz(rb, j) * 8);
+      const int rb2 = 128 * wn + 16 * x + m;
+      bfr[x] = *reinterpret_cast<const bf16x8*>(bs + rb2 * BK + tswz(rb2, j) * 8);
     }
 #pragma unroll
     for (int x = 0; x < 8; ++x)
 #pragma unroll
       for (int y = 0; y < 8; ++y)
         acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[x], bfr[y], acc[x][y], 0, 0, 0);
-    if (has_next) store(st ^ 1);
-    __syncthreads();
   }
 
   // Epilogue. acc[x][y][i] = C[row0 + 128 wm + 16x + 4j + i][col0 + 128 wn + 16y + m].
@@ -244,9 +283,18 @@ hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* w
   a.max_pos = max_pos;
   a.eps = eps;
   const int64_t mtiles = (rows + BM - 1) / BM;
-  const int64_t blocks = mtiles * (a.n / BN);
-  const size_t lds = 2 * 2 * (size_t)BM * BK * sizeof(bf16);
-  hipLaunchKernelGGL(ctx_kv_gemm_kernel, dim3((unsigned)blocks), dim3(NT), lds, s, a);
+  const int64_t blocks = (mtiles + 7) / 8 * 8 * (a.n / BN);  // whole groups of 8 row blocks
+  const size_t lds = (size_t)NSTAGE * 2 * BM * BK * sizeof(bf16);
+  static std::once_flag once[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::call_once(once[dev & 63], [] {
+    (void)hipFuncSetAttribute((const void*)ctx_kv_gemm_kernel,
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              NSTAGE * 2 * BM * BK * (int)sizeof(bf16));
+  });
+  if (blocks > 0)
+    hipLaunchKernelGGL(ctx_kv_gemm_kernel, dim3((unsigned)blocks), dim3(NT), lds, s, a);
   return hipGetLastError();
 }
 
