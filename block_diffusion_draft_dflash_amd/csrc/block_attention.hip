@@ -11,18 +11,23 @@
 // sources directly and computes block queries only.
 //
 // bf16 kernel (the hot path), one workgroup = 4 waves per work unit:
-//   unit = (request r, 64-row query tile, key range of `chunk` keys) x kv-head g
+//   unit = (request r, 64-row query tile, range of keys) x kv-head g
 //   query tile rows = the (G q-heads of kv-head g) x (block rows) pairs,
 //   flattened; wave w owns rows 16w..16w+15 (for G = 4, B = 16: q-head 4g+w).
-//   Per 64-key tile: K and V rows of head g are streamed HBM -> registers ->
-//   LDS (16-byte loads, XOR-swizzled rows, double buffered); S^T = K Q^T and
-//   O^T += V^T P^T run on v_mfma_f32_16x16x32_bf16; V^T operands come straight
-//   from the row-major V tile with ds_read_b64_tr_b16. Softmax is online in
-//   f32 (base-2 exponent, scale*log2(e) folded into one multiply); the four
-//   lanes that share a query row reduce with permlane swaps.
-//   A request whose key range spans several units writes f32 partials
-//   (unnormalised O, running max, sum); the last unit to finish (integer
-//   ticket per (request, query tile, kv-head)) merges them in split order, so
+//   Each request's visible keys are cut into equal splits (whole tiles),
+//   sized so that the units fill the machine; the plan is made on the host
+//   when host copies of the lengths are given, else by every workgroup from
+//   the device lengths. Per 32-key tile, the K and V rows of head g are
+//   copied HBM -> LDS directly (16-byte lanes, XOR-swizzled rows, NSTAGE
+//   stages, explicit waits); S^T = K Q^T and O^T += V^T P^T run on
+//   v_mfma_f32_16x16x32_bf16, the V^T operands read from the row-major V tile
+//   with ds_read_b64_tr_b16. Softmax is online in f32 (base-2 exponent,
+//   scale*log2(e) folded into one multiply, rescale only when a row max grows
+//   past a threshold); the four lanes that share a query row reduce with
+//   permlane swaps. With the fused prologue the raw q rows are normed and
+//   rotated in registers and the block's K rows in LDS.
+//   A unit of a split request writes its partial (O / l in fp16, max and sum
+//   in f32); a second kernel merges each request's splits in split order, so
 //   the result is deterministic.
 #include <algorithm>
 #include <mutex>
@@ -66,7 +71,7 @@ struct AttnArgs {
   const bf16* kc;
   const bf16* vc;
   bf16* out;
-  float* part_o;      // [units * hkv][QROWS][DH]
+  f16* part_o;        // [units * hkv][QROWS][DH]: O / l of each split (fp16)
   float* part_ml;     // [units * hkv][QROWS][2]
   int32_t* dir;       // [R][qtiles][hkv]: first unit index of each split set
   int64_t total_ctx, total_blk;
@@ -669,14 +674,22 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
     return;
   }
 
-  // Split: publish the partial (unnormalised O, reference max, sum). The
-  // merge kernel that follows on the stream combines the splits.
+  // Split: publish the partial: the split's own softmax output O / l in fp16
+  // (a convex combination of V rows, so within V's range; fp16 keeps 11
+  // significant bits, 8x finer than the bf16 output) with its reference max
+  // and sum in f32. The merge kernel that follows on the stream combines the
+  // splits.
   {
     const int64_t slot = (int64_t)u * a.hkv + g;
-    float* po = a.part_o + (slot * QROWS + nrow_unit) * DH + 4 * j;
+    f16* po = a.part_o + (slot * QROWS + nrow_unit) * DH + 4 * j;
+    const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      *reinterpret_cast<f32x4*>(po + 16 * dt) = acc_o[dt];
+    for (int dt = 0; dt < DT; ++dt) {
+      f16x4 h;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) h[i] = (f16)(acc_o[dt][i] * inv);
+      *reinterpret_cast<f16x4*>(po + 16 * dt) = h;
+    }
     if (j == 0) {
       float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot * QROWS + nrow_unit;
       *pml = make_float2(mx, ltot);
@@ -738,15 +751,13 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
     float M = -INFINITY, L = 0.f;
     for (int32_t s0 = 0; s0 < ns; s0 += MB) {
       float2 ml[MB];
-      f32x4 ov[MB][DV / 4];
+      f16x8 ov[MB];
 #pragma unroll
       for (int bb = 0; bb < MB; ++bb) {
         const int32_t sidx = s0 + bb < ns ? s0 + bb : ns - 1;
         const int64_t slot = (int64_t)(first + sidx) * a.hkv + g;
         ml[bb] = pml[slot * QROWS + row];
-        const f32x4* src = reinterpret_cast<const f32x4*>(a.part_o + (slot * QROWS + row) * DH + d0);
-#pragma unroll
-        for (int d = 0; d < DV / 4; ++d) ov[bb][d] = src[d];
+        ov[bb] = *reinterpret_cast<const f16x8*>(a.part_o + (slot * QROWS + row) * DH + d0);
       }
       float bm = M;
 #pragma unroll
@@ -759,15 +770,11 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
       for (int d = 0; d < DV; ++d) o[d] *= rescale;
 #pragma unroll
       for (int bb = 0; bb < MB; ++bb) {
-        const float wgt = (s0 + bb < ns) ? fast_exp2(ml[bb].x - bsafe) : 0.f;
-        L += ml[bb].y * wgt;
+        // split weight: its sum l times 2^(m - M); its values are O / l
+        const float wgt = (s0 + bb < ns) ? ml[bb].y * fast_exp2(ml[bb].x - bsafe) : 0.f;
+        L += wgt;
 #pragma unroll
-        for (int d = 0; d < DV / 4; ++d) {
-          o[4 * d] += ov[bb][d][0] * wgt;
-          o[4 * d + 1] += ov[bb][d][1] * wgt;
-          o[4 * d + 2] += ov[bb][d][2] * wgt;
-          o[4 * d + 3] += ov[bb][d][3] * wgt;
-        }
+        for (int d = 0; d < DV; ++d) o[d] += (float)ov[bb][d] * wgt;
       }
       M = bm;
     }
@@ -1021,7 +1028,7 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPl
   pl.off_counters = off;
   off = align_up(off + sizeof(int32_t) * (size_t)p.num_reqs * pl.qtiles * p.num_kv_heads, 256);
   pl.off_part_o = off;
-  off = align_up(off + sizeof(float) * (size_t)pl.units * p.num_kv_heads * QROWS * p.head_dim, 256);
+  off = align_up(off + sizeof(uint16_t) * (size_t)pl.units * p.num_kv_heads * QROWS * p.head_dim, 256);
   pl.off_part_ml = off;
   off = align_up(off + sizeof(float) * 2 * (size_t)pl.units * p.num_kv_heads * QROWS, 256);
   pl.bytes = (p.dtype == DFLASH_BF16) ? off : 0;
@@ -1055,7 +1062,7 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.kc = (const bf16*)kc; a.vc = (const bf16*)vc; a.out = (bf16*)out;
   char* w = (char*)ws;
   a.dir = (int32_t*)(w + plan.off_counters);
-  a.part_o = (float*)(w + plan.off_part_o);
+  a.part_o = (f16*)(w + plan.off_part_o);
   a.part_ml = (float*)(w + plan.off_part_ml);
   a.total_ctx = p.total_ctx; a.total_blk = p.total_blk;
   a.num_reqs = p.num_reqs; a.hq = p.num_q_heads; a.hkv = p.num_kv_heads;

@@ -183,9 +183,12 @@ dflash_status dflash_block_attention_check(const dflash_block_attn_params* p);
  *   k_ctx   [total_ctx, Hkv, Dh], v_ctx alike; may be NULL if total_ctx == 0.
  *   out     [total_blk, Hq, Dh], written (rows of empty requests untouched).
  *   workspace  device, 256-byte aligned, >= dflash_block_attention_workspace_size
- *           bytes (no initialisation needed). It holds the f32 partial results
- *           of key ranges that were split across work units; one workspace must
- *           not be used by two calls that may run concurrently.
+ *           bytes (no initialisation needed). It holds the partial results of
+ *           key ranges that were split across work units (each split's
+ *           softmax output in fp16, its max and sum in f32); one workspace
+ *           must not be used by two calls that may run concurrently. Split
+ *           partials are convex combinations of V rows: |V| must stay within
+ *           the fp16 range (65504), far above bf16 activations in practice.
  * The result does not depend on how the keys are split into work units other
  * than through f32 rounding; for a fixed split_keys it is bitwise
  * deterministic.
