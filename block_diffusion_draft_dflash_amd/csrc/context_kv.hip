@@ -10,12 +10,16 @@
 //   K[t, o] = (1 / rms_t) * sum_j h[t, j] * (hidden_norm[j] * W_k[o, j]),
 // so the weights are pre-multiplied by hidden_norm once per call (rounded to
 // bf16, the reference rounds the normed activations instead) and 1/rms_t is
-// applied in the GEMM epilogue. The GEMM (M = rows, N = 2 * Hkv * Dh, K = H)
-// runs on v_mfma_f32_16x16x32_bf16 with 256x256 workgroup tiles; each wave owns
-// 128 rows x one 128-wide head, so the k-norm and the rotate-half pairs
-// (d, d + 64) are resolved in registers of one wave. The k-slices of A and B
-// are copied HBM -> LDS directly (no register staging), NSTAGE - 1 slices
-// ahead, with explicit waits and fence-free barriers.
+// applied in the GEMM epilogue; the GEMM computes it from the A fragments
+// its waves already hold (no separate pass over the hidden states). The GEMM (M = rows, N = 2 * Hkv * Dh, K = H)
+// runs on v_mfma_f32_16x16x32_bf16 with 256x256 workgroup tiles of 8 waves
+// (two per SIMD); a wave owns 128 rows x 64 columns of one 128-wide head,
+// chosen so that the rotate-half pairs (d, d + 64) meet in one lane; the
+// k-norm's sum of squares is completed with the partner wave through LDS.
+// The k-slices of A and B are copied HBM -> LDS directly (no register
+// staging) up to NSTAGE slices ahead, with explicit waits and fence-free
+// barriers, and each wave reads the next slice's fragments while the MFMAs
+// of the current one run.
 #include <mutex>
 
 #include "dflash_device.h"
@@ -24,7 +28,7 @@
 namespace dflash {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256;
+constexpr int BM = 256, BN = 256, BK = 32;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -49,31 +53,9 @@ __global__ __launch_bounds__(256) void fold_weights_kernel(const bf16* __restric
   *reinterpret_cast<bf16x8*>(wout + idx) = o;
 }
 
-// rstd[t] = 1 / sqrt(mean(h[t]^2) + eps); one wave per row.
-__global__ __launch_bounds__(256) void row_rstd_kernel(const bf16* __restrict__ h,
-                                                       float* __restrict__ rstd, int64_t rows,
-                                                       int32_t hidden, float eps) {
-  const int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / 64;
-  const int lane = threadIdx.x & 63;
-  if (row >= rows) return;
-  const bf16* p = h + row * hidden;
-  float ss = 0.f;
-  for (int32_t c = lane * 8; c < hidden; c += 512) {
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(p + c);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = bf2f(v[e]);
-      ss += x * x;
-    }
-  }
-  ss = group_sum<64>(ss);
-  if (lane == 0) rstd[row] = 1.0f / sqrtf(ss / (float)hidden + eps);
-}
-
 struct CkvArgs {
   const bf16* h;        // [rows, H]
   const bf16* w;        // [N, H] folded weights, K rows then V rows
-  const float* rstd;    // [rows]
   const float* knw;     // [Dh]
   const int32_t* pos;   // [rows]
   const float2* table;  // [max_pos][Dh/2]
@@ -106,18 +88,20 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(NT) void ctx_kv_gemm_kernel(CkvArgs a) {
+constexpr int NTG = 512;  // GEMM workgroup: 8 waves, two per SIMD
+
+__global__ __launch_bounds__(NTG) void ctx_kv_gemm_kernel(CkvArgs a) {
   constexpr int DH = 128;
   constexpr int HALF = DH / 2;
-  constexpr int TILE = BM * BK;         // elements per A (or B) k-slice
-  constexpr int CPW = TILE / 512 / 4;   // 1 KB copies per wave per operand per k-slice (4)
-  constexpr int CPS = 2 * CPW;          // per thread per k-slice (A and B)
+  constexpr int TILE = BM * BK;               // elements per A (or B) k-slice
+  constexpr int NW = NTG / 64;
+  constexpr int CPW = TILE / 512 / NW;        // 1 KB copies per wave per operand per k-slice (2)
+  constexpr int CPS = 2 * CPW;                // per thread per k-slice (A and B)
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][A | B]
 
   // Block order: the dispatcher deals workgroups to the 8 XCDs round-robin.
   // Consecutive row blocks go to different XCDs and each XCD runs all column
-  // tiles of its row blocks, so an XCD's L2 fetches each A row block once
-  // (B, 16 MB at most, is shared through the last-level cache).
+  // tiles of its row blocks.
   const int ntn = a.n / BN;
   const int xcd = blockIdx.x % 8;
   const int slot = blockIdx.x / 8;
@@ -127,12 +111,13 @@ __global__ __launch_bounds__(NT) void ctx_kv_gemm_kernel(CkvArgs a) {
   const int col0 = (slot % ntn) * BN;
   const int tid = threadIdx.x;
   const int w = tid >> 6, lane = tid & 63, m = lane & 15, j = lane >> 4;
-  const int wm = w >> 1, wn = w & 1;
+  // Wave tile: 128 rows (half wm) x 64 columns of head hw of the tile: the
+  // 32-column chunks cc and cc + 2 of the head (columns d and d + 64 of a
+  // rotate-half pair are in the same lane); the partner wave (w ^ 2) holds
+  // the head's other 64 columns.
+  const int wm = w & 1, wn = w >> 1, hw = wn >> 1, cc = wn & 1;
+  auto hcol = [&](int y) { return (y >> 1) * HALF + cc * 32 + (y & 1) * 16; };  // column in head
 
-  // Copies: one wave-wide 16-byte-per-lane load fills 1 KB = 16 tile rows of
-  // LDS in lane order; lane L takes the logical chunk the swizzle stores at
-  // its slot. Rows past the end re-read the last row (their results are not
-  // stored).
   const bf16* asrc[CPW];
   const bf16* bsrc[CPW];
 #pragma unroll
@@ -162,85 +147,170 @@ __global__ __launch_bounds__(NT) void ctx_kv_gemm_kernel(CkvArgs a) {
     }
   };
 
-  f32x4 acc[8][8];
+  f32x4 acc[8][4];
 #pragma unroll
   for (int x = 0; x < 8; ++x)
 #pragma unroll
-    for (int y = 0; y < 8; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int32_t ksteps = a.hidden / BK;
-#pragma unroll
-  for (int t = 0; t < NSTAGE - 1; ++t)
-    if (t < ksteps) issue(t);
-  for (int32_t ks = 0; ks < ksteps; ++ks) {
-    // own copies of slice ks landed (later slices may stay in flight); the
-    // barrier publishes every wave's part and frees the stage of slice ks-1
-    const int32_t after = min(ksteps - 1 - ks, NSTAGE - 2);
-    if (after >= 2) wait_vmcnt<2 * CPS>();
-    else if (after == 1) wait_vmcnt<CPS>();
-    else wait_vmcnt<0>();
-    block_barrier();
-    if (ks + NSTAGE - 1 < ksteps) issue(ks + NSTAGE - 1);
+  auto read_frags = [&](int32_t ks, bf16x8 (&af)[8], bf16x8 (&bfr)[4]) {
     const bf16* as = smem + (ks % NSTAGE) * 2 * TILE;
     const bf16* bs = as + TILE;
-    bf16x8 af[8], bfr[8];
 #pragma unroll
     for (int x = 0; x < 8; ++x) {
       const int ra = 128 * wm + 16 * x + m;
       af[x] = *reinterpret_cast<const bf16x8*>(as + ra * BK + tswz(ra, j) * 8);
-      const int rb2 = 128 * wn + 16 * x + m;
-      bfr[x] = *reinterpret_cast<const bf16x8*>(bs + rb2 * BK + tswz(rb2, j) * 8);
     }
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int rbb = hw * DH + hcol(y) + m;
+      bfr[y] = *reinterpret_cast<const bf16x8*>(bs + rbb * BK + tswz(rbb, j) * 8);
+    }
+  };
+  auto mma = [&](const bf16x8 (&af)[8], const bf16x8 (&bfr)[4]) {
 #pragma unroll
     for (int x = 0; x < 8; ++x)
 #pragma unroll
-      for (int y = 0; y < 8; ++y)
+      for (int y = 0; y < 4; ++y)
         acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[x], bfr[y], acc[x][y], 0, 0, 0);
+  };
+  // wait until this thread's copies of slice t landed, given the last slice issued
+  auto wait_slice = [&](int32_t t, int32_t last) {
+    const int32_t after = min(last - t, NSTAGE - 1);
+    if (after >= 3) wait_vmcnt<3 * CPS>();
+    else if (after == 2) wait_vmcnt<2 * CPS>();
+    else if (after == 1) wait_vmcnt<CPS>();
+    else wait_vmcnt<0>();
+  };
+  auto lgkm0 = [] { __builtin_amdgcn_s_waitcnt(0xC07F); };
+
+  const int32_t ksteps = a.hidden / BK;
+  auto read_a = [&](int32_t ks, bf16x8 (&af)[8]) {
+    const bf16* as = smem + (ks % NSTAGE) * 2 * TILE;
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const int ra = 128 * wm + 16 * x + m;
+      af[x] = *reinterpret_cast<const bf16x8*>(as + ra * BK + tswz(ra, j) * 8);
+    }
+  };
+  auto read_b = [&](int32_t ks, bf16x8 (&bfr)[4]) {
+    const bf16* bs = smem + (ks % NSTAGE) * 2 * TILE + TILE;
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int rbb = hw * DH + hcol(y) + m;
+      bfr[y] = *reinterpret_cast<const bf16x8*>(bs + rbb * BK + tswz(rbb, j) * 8);
+    }
+  };
+  int32_t last = -1;
+#pragma unroll
+  for (int t = 0; t < NSTAGE; ++t)
+    if (t < ksteps) { issue(t); last = t; }
+  bf16x8 fa[8], fb[4], gb[4];
+  float hsq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // hidden row sums of squares (wn == 0)
+  wait_slice(0, last);
+  block_barrier();
+  read_b(0, fb);
+  for (int32_t ks = 0; ks < ksteps; ++ks) {
+    read_a(ks, fa);
+    // B of slice ks in fb; A of slice ks read above; B of ks+1 under the MFMAs
+    if (ks + 1 < ksteps) {
+      wait_slice(ks + 1, last);
+      lgkm0();
+      block_barrier();
+      if (ks + NSTAGE < ksteps) { issue(ks + NSTAGE); last = ks + NSTAGE; }
+      read_b(ks + 1, gb);
+    }
+    mma(fa, fb);
+    if (wn == 0) {
+#pragma unroll
+      for (int x = 0; x < 8; ++x)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = bf2f(fa[x][e]);
+          hsq[x] += v * v;
+        }
+    }
+#pragma unroll
+    for (int y = 0; y < 4; ++y) fb[y] = gb[y];
   }
 
-  // Epilogue. acc[x][y][i] = C[row0 + 128 wm + 16x + 4j + i][col0 + 128 wn + 16y + m].
-  const int head = (col0 + 128 * wn) / DH;  // 0..2*Hkv-1: K heads first, then V heads
-  const bool is_k = head < a.hkv;
+  // Row scale of the hidden RMSNorm, from the A fragments the wn == 0 waves
+  // consumed: 1 / sqrt(mean(h^2) + eps) per row, shared through LDS.
+  float* rst = reinterpret_cast<float*>(smem) + NW * 128;  // [256]
+  lgkm0();
+  block_barrier();  // every wave is done with the stages
+  if (wn == 0) {
+#pragma unroll
+    for (int x = 0; x < 8; ++x) {
+      const float ss = xrow4_sum(hsq[x]);  // the 4 lane groups cover the row's k chunks
+      if (j == 0) rst[128 * wm + 16 * x + m] = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
+    }
+  }
+  lgkm0();
+  block_barrier();
+  // Epilogue. acc[x][y][i] = C[row0 + 128 wm + 16x + 4j + i][col0 + 128 hw + hcol(y) + m].
+  const int head = (col0 + DH * hw) / DH;  // 0..2*Hkv-1: K heads first, then V heads
+  const bool is_k = col0 < a.hkv * DH;     // a 256-column tile is all K or all V
   bf16* dst_base = is_k ? a.k_out : a.v_out;
   const int hh = is_k ? head : head - a.hkv;
-  float kw[8];
+  if (is_k) {
+    // per-head RMSNorm: this wave's 64 columns of each row, then the partner's
+    float* sq = reinterpret_cast<float*>(smem);  // [NW][128]
 #pragma unroll
-  for (int y = 0; y < 8; ++y) kw[y] = a.knw[16 * y + m];
+    for (int x = 0; x < 8; ++x)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t row = row0 + 128 * wm + 16 * x + 4 * j + i;
+        const float rs = row < a.rows ? rst[128 * wm + 16 * x + 4 * j + i] : 0.f;
+        float ss = 0.f;
+#pragma unroll
+        for (int y = 0; y < 4; ++y) {
+          const float v = acc[x][y][i] * rs;
+          ss += v * v;
+        }
+        ss = group_sum<16>(ss);  // the 16 lanes of group j hold this row's 64 columns
+        if (m == 0) sq[w * 128 + 16 * x + 4 * j + i] = ss;
+      }
+    lgkm0();
+    block_barrier();
+  }
+  float kw[4];
+#pragma unroll
+  for (int y = 0; y < 4; ++y) kw[y] = a.knw[hcol(y) + m];
 #pragma unroll
   for (int x = 0; x < 8; ++x) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t row = row0 + 128 * wm + 16 * x + 4 * j + i;
+      const int rloc = 16 * x + 4 * j + i;
+      const int64_t row = row0 + 128 * wm + rloc;
       const bool rv = row < a.rows;
-      const float rs = rv ? a.rstd[row] : 0.f;
-      float y8[8];
+      const float rs = rv ? rst[rloc + 128 * wm] : 0.f;
+      float y4[4];
 #pragma unroll
-      for (int y = 0; y < 8; ++y) y8[y] = acc[x][y][i] * rs;
+      for (int y = 0; y < 4; ++y) y4[y] = acc[x][y][i] * rs;
       if (is_k) {
-        float ss = 0.f;
-#pragma unroll
-        for (int y = 0; y < 8; ++y) ss += y8[y] * y8[y];
-        ss = group_sum<16>(ss);  // the 16 lanes of group j hold this row's 128 columns
+        const float* sq = reinterpret_cast<const float*>(smem);
+        const float ss = sq[w * 128 + rloc] + sq[(w ^ 2) * 128 + rloc];
         const float inv = 1.0f / sqrtf(ss * (1.0f / DH) + a.eps);
 #pragma unroll
-        for (int y = 0; y < 8; ++y) y8[y] *= inv * kw[y];
+        for (int y = 0; y < 4; ++y) y4[y] *= inv * kw[y];
         if (rv) {
           int32_t p = a.pos[row];
           p = p < 0 ? 0 : (p >= a.max_pos ? a.max_pos - 1 : p);
-          const float2* cs = a.table + (int64_t)p * HALF + m;
+          const float2* cs = a.table + (int64_t)p * HALF;
 #pragma unroll
-          for (int y = 0; y < 4; ++y) {
-            const float2 c = cs[16 * y];
-            const float lo = y8[y], hi = y8[y + 4];
-            y8[y] = lo * c.x - hi * c.y;
-            y8[y + 4] = hi * c.x + lo * c.y;
+          for (int y = 0; y < 2; ++y) {  // pairs (d, d + 64): y and y + 2
+            const float2 c = cs[hcol(y) + m];
+            const float lo = y4[y], hi = y4[y + 2];
+            y4[y] = lo * c.x - hi * c.y;
+            y4[y + 2] = hi * c.x + lo * c.y;
           }
         }
       }
       if (rv) {
         bf16* dst = dst_base + (row * a.hkv + hh) * DH + m;
 #pragma unroll
-        for (int y = 0; y < 8; ++y) dst[16 * y] = f2bf(y8[y]);
+        for (int y = 0; y < 4; ++y) dst[hcol(y)] = f2bf(y4[y]);
       }
     }
   }
@@ -249,7 +319,8 @@ __global__ __launch_bounds__(NT) void ctx_kv_gemm_kernel(CkvArgs a) {
 }  // namespace
 
 size_t context_kv_workspace_bytes(int64_t rows, int32_t hidden, int32_t hkv, int32_t dh) {
-  return align256((size_t)2 * hkv * dh * hidden * sizeof(bf16)) + align256((size_t)rows * sizeof(float));
+  (void)rows;
+  return align256((size_t)2 * hkv * dh * hidden * sizeof(bf16));
 }
 
 hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* wk,
@@ -259,18 +330,15 @@ hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* w
                              void* ws, hipStream_t s) {
   const int64_t kdim = (int64_t)hkv * dh;
   bf16* wfold = (bf16*)ws;
-  float* rstd = (float*)((char*)ws + align256((size_t)2 * kdim * hidden_size * sizeof(bf16)));
   {
     const int64_t n8 = 2 * kdim * hidden_size / 8;
     hipLaunchKernelGGL(fold_weights_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
                        (const bf16*)wk, (const bf16*)wv, hnw, wfold, kdim, hidden_size);
   }
-  hipLaunchKernelGGL(row_rstd_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, s,
-                     (const bf16*)hidden, rstd, rows, hidden_size, eps);
+
   CkvArgs a{};
   a.h = (const bf16*)hidden;
   a.w = wfold;
-  a.rstd = rstd;
   a.knw = knw;
   a.pos = pos;
   a.table = reinterpret_cast<const float2*>(table);
@@ -294,7 +362,7 @@ hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* w
                               NSTAGE * 2 * BM * BK * (int)sizeof(bf16));
   });
   if (blocks > 0)
-    hipLaunchKernelGGL(ctx_kv_gemm_kernel, dim3((unsigned)blocks), dim3(NT), lds, s, a);
+    hipLaunchKernelGGL(ctx_kv_gemm_kernel, dim3((unsigned)blocks), dim3(NTG), lds, s, a);
   return hipGetLastError();
 }
 

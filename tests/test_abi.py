@@ -149,7 +149,7 @@ def test_workspace_sizes(lib):
 
 def test_context_kv_workspace_size(lib):
     n = B.dflash_context_kv_workspace_size(131072, 4096, 8, 128)
-    assert n >= 2 * 1024 * 4096 * 2 + 131072 * 4
+    assert n >= 2 * 1024 * 4096 * 2  # the folded K and V weights (bf16)
     assert B.dflash_context_kv_workspace_size(-1, 4096, 8, 128) == 0
 
 
