@@ -206,7 +206,7 @@ __global__ __launch_bounds__(NTG) void ctx_kv_gemm_kernel(CkvArgs a) {
   for (int t = 0; t < NSTAGE; ++t)
     if (t < ksteps) { issue(t); last = t; }
   bf16x8 fa[8], fb[4], gb[4];
-  float hsq[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};  // hidden row sums of squares (wn == 0)
+  float hsq[2] = {0.f, 0.f};  // hidden row sums of squares, row blocks 2wn and 2wn + 1
   wait_slice(0, last);
   block_barrier();
   read_b(0, fb);
@@ -221,30 +221,30 @@ __global__ __launch_bounds__(NTG) void ctx_kv_gemm_kernel(CkvArgs a) {
       read_b(ks + 1, gb);
     }
     mma(fa, fb);
-    if (wn == 0) {
+    // the four waves that share these A rows split the row sums: wave wn takes
+    // row blocks 2wn, 2wn + 1 (selected without dynamic register indexing)
 #pragma unroll
-      for (int x = 0; x < 8; ++x)
+    for (int x = 0; x < 8; ++x)
+      if ((x >> 1) == wn) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const float v = bf2f(fa[x][e]);
-          hsq[x] += v * v;
+          hsq[x & 1] += v * v;
         }
-    }
+      }
 #pragma unroll
     for (int y = 0; y < 4; ++y) fb[y] = gb[y];
   }
 
-  // Row scale of the hidden RMSNorm, from the A fragments the wn == 0 waves
-  // consumed: 1 / sqrt(mean(h^2) + eps) per row, shared through LDS.
+  // Row scale of the hidden RMSNorm, from the A fragments the waves consumed:
+  // 1 / sqrt(mean(h^2) + eps) per row, shared through LDS.
   float* rst = reinterpret_cast<float*>(smem) + NW * 128;  // [256]
   lgkm0();
   block_barrier();  // every wave is done with the stages
-  if (wn == 0) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const float ss = xrow4_sum(hsq[x]);  // the 4 lane groups cover the row's k chunks
-      if (j == 0) rst[128 * wm + 16 * x + m] = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
-    }
+  for (int h = 0; h < 2; ++h) {
+    const float ss = xrow4_sum(hsq[h]);  // the 4 lane groups cover the row's k chunks
+    if (j == 0) rst[128 * wm + 16 * (2 * wn + h) + m] = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
   }
   lgkm0();
   block_barrier();

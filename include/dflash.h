@@ -122,9 +122,11 @@ typedef struct {
   /* Optional HOST copies of cu_ctx_lens / cu_blk_lens (int32 [R+1] each, equal
    * to the device arrays; both or neither). With them the split of the keys
    * into work units is planned on the host and handed to the kernels with the
-   * launch (up to 64 requests and 512 units per kv-head; beyond that, and when
-   * NULL, the kernels plan it from the device arrays; the result is the same
-   * either way). They are read during the call only; under stream capture the
+   * launch (up to 64 requests, 512 units per kv-head and 256 per request;
+   * beyond that, and when NULL, the kernels plan it from the device arrays;
+   * the result is bitwise the same either way). The bf16 kernels then take
+   * the row ranges from these copies (the f32 path always reads the device
+   * arrays). They are read during the call only; under stream capture the
    * plan is fixed into the graph, so the lengths must not change between
    * replays. Checked: [0] = 0, nondecreasing, cu_ctx_lens[R] = total_ctx,
    * cu_blk_lens[R] = total_blk, block lengths <= max_blk_len. The pages build
