@@ -112,6 +112,8 @@ def main() -> int:
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true",
                     help="q/k norm + RoPE as a separate in-place call before the attention")
+    ap.add_argument("--paged", action="store_true",
+                    help="read the context from a paged store (dflash_block_attention_paged)")
     ap.add_argument("--device-plan", action="store_true",
                     help="leave the work split to the kernels (no host copies of the lengths)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
@@ -143,7 +145,8 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
     wl = make_workload(args.workload)
-    paths = [DevicePath(wl, split_keys=args.split_keys, host_lengths=not args.device_plan)
+    paths = [DevicePath(wl, split_keys=args.split_keys, host_lengths=not args.device_plan,
+                        paged=args.paged)
              for _ in range(args.rotate)]
     for p in paths:
         p.prepare_context()
@@ -276,12 +279,14 @@ def main() -> int:
             "hip_graph": use_graph,
             "fused_qk_norm_rope": fused,
             "work_split": "device-planned" if args.device_plan else "host-planned",
+            "context_store": "paged (16-row pages)" if args.paged else "packed",
         },
         "draft_query_tokens_per_s": tokens_per_s,
         "roofline": {
             "bound": "hbm",
-            "kernel": ("dflash_block_attention call = block_attn_bf16_kernel%s + "
-                       "block_attn_merge_kernel" % (" (fused q/k norm + RoPE)" if fused else "")),
+            "kernel": ("dflash_block_attention%s call = block_attn_bf16_kernel%s + "
+                       "block_attn_merge_kernel" % ("_paged" if args.paged else "",
+                                                    " (fused q/k norm + RoPE)" if fused else "")),
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",

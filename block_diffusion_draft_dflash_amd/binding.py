@@ -35,6 +35,9 @@ EXPORTED = (
     "dflash_block_attention",
     "dflash_context_kv_workspace_size",
     "dflash_context_kv",
+    "dflash_block_attention_paged",
+    "dflash_block_attention_paged_workspace_size",
+    "dflash_kv_scatter",
 )
 
 
@@ -78,6 +81,17 @@ class QkPrologue(ctypes.Structure):
     ]
 
 
+class PagedCtx(ctypes.Structure):
+    """Mirror of ``dflash_paged_ctx``."""
+
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("max_pages_per_req", ctypes.c_int32),
+        ("page_size", ctypes.c_int32),
+        ("num_pages", ctypes.c_int64),
+    ]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -112,6 +126,15 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dflash_context_kv_workspace_size.argtypes = [I64, I32, I32, I32]
     lib.dflash_context_kv.restype = ctypes.c_int
     lib.dflash_context_kv.argtypes = [P, P, P, P, P, P, I64, I32, I32, I32, F, P, I32, P, P, P, SZ, P]
+    lib.dflash_block_attention_paged.restype = ctypes.c_int
+    lib.dflash_block_attention_paged.argtypes = [ctypes.POINTER(BlockAttnParams),
+                                                 ctypes.POINTER(PagedCtx),
+                                                 ctypes.POINTER(QkPrologue), P, P, P, P, P, P, P,
+                                                 P, P, SZ, P]
+    lib.dflash_block_attention_paged_workspace_size.restype = SZ
+    lib.dflash_block_attention_paged_workspace_size.argtypes = [ctypes.POINTER(BlockAttnParams)]
+    lib.dflash_kv_scatter.restype = ctypes.c_int
+    lib.dflash_kv_scatter.argtypes = [ctypes.c_int, P, P, P, I64, I32, I32, P, P, I64, P]
     _lib = lib
     return lib
 
@@ -249,3 +272,41 @@ def alloc_workspace(nbytes: int, device="cuda") -> Optional[torch.Tensor]:
     if nbytes == 0:
         return None
     return torch.zeros((nbytes + 255) // 256 * 256, dtype=torch.uint8, device=device)
+
+
+def make_paged_ctx(block_table: torch.Tensor, num_pages: int, page_size: int = 16) -> PagedCtx:
+    """``block_table``: device int32 [num_reqs, max_pages_per_req]."""
+    if block_table.dtype != torch.int32 or block_table.dim() != 2:
+        raise ValueError("block_table must be a 2-D int32 tensor")
+    return PagedCtx(_ptr(block_table), block_table.shape[1], page_size, num_pages)
+
+
+def dflash_block_attention_paged_workspace_size(p: BlockAttnParams) -> int:
+    return load().dflash_block_attention_paged_workspace_size(ctypes.byref(p))
+
+
+def dflash_block_attention_paged(p: BlockAttnParams, pg: PagedCtx, cu_ctx_lens: torch.Tensor,
+                                 cu_blk_lens: torch.Tensor, q: torch.Tensor, k_blk: torch.Tensor,
+                                 v_blk: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor,
+                                 out: torch.Tensor, workspace: Optional[torch.Tensor], stream=None,
+                                 prologue: Optional[QkPrologue] = None) -> None:
+    """Block attention over a paged context store (pools ``[pages, 16, Hkv, Dh]``)."""
+    lib = load()
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dflash_block_attention_paged(ctypes.byref(p), ctypes.byref(pg),
+                                            ctypes.byref(prologue) if prologue is not None else None,
+                                            _ptr(cu_ctx_lens), _ptr(cu_blk_lens), _ptr(q),
+                                            _ptr(k_blk), _ptr(v_blk), _ptr(k_pool), _ptr(v_pool),
+                                            _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dflash_kv_scatter(k_src: torch.Tensor, v_src: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_pool: torch.Tensor, v_pool: torch.Tensor, stream=None) -> None:
+    """Rows of ``k_src``/``v_src`` ``[T, Hkv, Dh]`` to pool slots (pools viewed as
+    ``[slots, Hkv, Dh]``); slots outside the pool (e.g. -1) are skipped."""
+    lib = load()
+    t, hkv, dh = k_src.shape
+    num_slots = k_pool.numel() // (hkv * dh)
+    _check(lib.dflash_kv_scatter(_dtype_code(k_src), _ptr(k_src), _ptr(v_src), _ptr(slot_mapping),
+                                 t, hkv, dh, _ptr(k_pool), _ptr(v_pool), num_slots,
+                                 _stream(stream)))

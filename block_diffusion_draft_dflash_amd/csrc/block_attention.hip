@@ -39,6 +39,9 @@ namespace dflash {
 namespace {
 
 constexpr int QROWS = 64;  // query rows per work unit
+constexpr int PAGE = 16;   // rows per page of the paged context store
+constexpr int PAGED_MAX_UNIT_KEYS = 16384;             // keys per unit over a paged store
+constexpr int PG_MAX = PAGED_MAX_UNIT_KEYS / PAGE + 64;  // page ids a unit stages in LDS
 constexpr int KT = 32;     // keys per tile
 constexpr int NT = 256;    // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
@@ -79,6 +82,11 @@ struct AttnArgs {
   int32_t num_reqs, hq, hkv, group, qtiles, max_blk;
   int32_t chunk;      // keys per split (multiple of KT), or 0: chosen on the device
   int32_t units;      // work units per kv-head in the grid (grid = units * hkv)
+  int32_t units_pref; // unit budget tried first (the packed call's; <= units)
+  // Paged context store (bt == nullptr: packed context rows).
+  const int32_t* bt;  // [num_reqs][bt_stride] page ids
+  int32_t bt_stride;
+  int32_t num_pages_m1;  // num_pages - 1 (clamped to int32)
   // Fused q/k prologue (q and k_blk raw): per-head RMSNorm + NeoX RoPE.
   const float* qnw;     // [Dh]
   const float* knw;     // [Dh]
@@ -173,8 +181,17 @@ struct ReqView {
 // of equal-sized units. Every workgroup computes the same value from the same
 // lengths. The host guarantees a.units >= sum of nq_r, i.e. one unit per
 // (request, query tile) always fits.
+__device__ int32_t choose_chunk_for(const AttnArgs& a, const ReqView& rv, int32_t units);
+// Over a paged store a unit spans at most PAGED_MAX_UNIT_KEYS keys (its page
+// ids are staged in LDS): the packed call's budget is tried first, so the two
+// calls split alike whenever that fits.
 __device__ int32_t choose_chunk(const AttnArgs& a, const ReqView& rv) {
   if (a.chunk > 0) return a.chunk;
+  const int32_t c = choose_chunk_for(a, rv, a.units_pref);
+  if (a.bt == nullptr || c <= PAGED_MAX_UNIT_KEYS || a.units_pref >= a.units) return c;
+  return choose_chunk_for(a, rv, a.units);
+}
+__device__ int32_t choose_chunk_for(const AttnArgs& a, const ReqView& rv, int32_t units) {
   auto count = [&](int32_t c) {
     int64_t tot = 0;
     for (int32_t r0 = 0; r0 < a.num_reqs; r0 += 64) {
@@ -191,19 +208,19 @@ __device__ int32_t choose_chunk(const AttnArgs& a, const ReqView& rv) {
     work += wave_sum64((int64_t)((q.n + KT - 1) / KT) * q.nq);  // in tiles
   }
   const int32_t kmax = max(1, (maxn + KT - 1) / KT);
-  int32_t klo = (int32_t)max((int64_t)1, min((int64_t)kmax, (work + a.units - 1) / max(a.units, 1)));
-  if (count(klo * KT) <= a.units) return klo * KT;
+  int32_t klo = (int32_t)max((int64_t)1, min((int64_t)kmax, (work + units - 1) / max(units, 1)));
+  if (count(klo * KT) <= units) return klo * KT;
   // grow geometrically, then bisect: count() is non-increasing in c
   int32_t khi = klo, step = 1;
   while (khi < kmax) {
     khi = min(kmax, khi + step);
     step *= 2;
-    if (count(khi * KT) <= a.units) break;
+    if (count(khi * KT) <= units) break;
     klo = khi;
   }
   while (khi - klo > 1) {
     const int32_t mid = (klo + khi) / 2;
-    if (count(mid * KT) <= a.units) khi = mid; else klo = mid;
+    if (count(mid * KT) <= units) khi = mid; else klo = mid;
   }
   return khi * KT;
 }
@@ -333,12 +350,26 @@ __device__ __forceinline__ void norm_rope_frag(const bf16x8 (&xin)[DH / 32], con
   }
 }
 
+// Pool row of context key k of a unit over a paged store, from the page ids
+// the unit staged in LDS (s_pg[i] = page of keys [PAGE (pfirst + i), ...));
+// both the LDS index and the page id are clamped into range.
+__device__ __forceinline__ int64_t paged_row(const int32_t* s_pg, int32_t k, int32_t pfirst,
+                                             int32_t num_pages_m1) {
+  const int32_t i = min(max(k / PAGE - pfirst, 0), PG_MAX - 1);
+  const int32_t pid = min(max(s_pg[i], 0), num_pages_m1);
+  return (int64_t)pid * PAGE + (k % PAGE);
+}
+
 __device__ __forceinline__ int32_t clamp_pos(int32_t p, int32_t max_pos) {
   return p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
 }
 
+// Two workgroups (8 waves) per CU at this kernel's LDS use, so up to 256
+// VGPRs per wave are free; saying so keeps the compiler from spilling to
+// stay under the 4-wave budget (a scratch reload inside the loop would wait
+// for every tile copy in flight).
 template <int DH, bool FUSE>
-__global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void block_attn_bf16_kernel(AttnArgs a) {
   constexpr int CH = DH / 8;                 // 16-byte chunks per row
   constexpr int DS = DH / 32;                // MFMA k-steps over the head dim
   constexpr int DT = DH / 16;                // 16-wide d tiles of O^T
@@ -453,6 +484,15 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
     koff[i] = lrow[i] * rstride + swz_k<DH>(lrow[i], lane % CH) * 8;
     voff[i] = lrow[i] * rstride + swz_v<DH>(lrow[i], lane % CH) * 8;
   }
+  // Paged context: the unit's page ids are staged in LDS (after the stages)
+  // before the first tile copy; context row k of the unit then lives at pool
+  // row s_pg[k / PAGE - pfirst] * PAGE + k % PAGE.
+  const bool paged = a.bt != nullptr;
+  int32_t* const s_pg = reinterpret_cast<int32_t*>(smem + NSTAGE * STAGE_ELEMS);
+  const int32_t kc_end = min(k_end, un.clen);
+  const int32_t pfirst = k_begin / PAGE;
+  const int32_t npg = (paged && kc_end > k_begin) ? (kc_end - 1) / PAGE - pfirst + 1 : 0;
+  const int32_t ctx0 = un.ctx0, np_m1 = a.num_pages_m1;
   // The copies are issued through inline assembly: the compiler's wait
   // insertion cannot tell which LDS stage a later LDS read touches and would
   // otherwise drain every copy in flight before it. All waits on these copies
@@ -470,12 +510,22 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
     const int32_t kt0 = tile_k0(t);
     bf16* st = smem + (t % NSTAGE) * STAGE_ELEMS;
     if (kt0 + KT <= min(un.clen, k_end)) {
-      const int64_t base = (int64_t)(un.ctx0 + kt0) * rstride;
+      if (!paged) {
+        const int64_t base = (int64_t)(un.ctx0 + kt0) * rstride;
 #pragma unroll
-      for (int i = 0; i < LPW; ++i) {
-        const int q = w * LPW + i;
-        dma(kc_g + base + koff[i], st + q * 512);
-        dma(vc_g + base + voff[i], st + TILE_ELEMS + q * 512);
+        for (int i = 0; i < LPW; ++i) {
+          const int q = w * LPW + i;
+          dma(kc_g + base + koff[i], st + q * 512);
+          dma(vc_g + base + voff[i], st + TILE_ELEMS + q * 512);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < LPW; ++i) {
+          const int q = w * LPW + i;
+          const int64_t rbase = (paged_row(s_pg, kt0 + lrow[i], pfirst, np_m1) - lrow[i]) * rstride;
+          dma(kc_g + rbase + koff[i], st + q * 512);
+          dma(vc_g + rbase + voff[i], st + TILE_ELEMS + q * 512);
+        }
       }
     } else if (kt0 >= un.clen && kt0 + KT <= k_end) {
       const int64_t base = (int64_t)(un.blk0 + kt0 - un.clen) * rstride;
@@ -491,10 +541,15 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
         const int q = w * LPW + i;
         const int32_t kidx = min(kt0 + lrow[i], k_end - 1);
         const bool in_ctx = kidx < un.clen;
-        const int32_t r = in_ctx ? un.ctx0 + kidx : un.blk0 + (kidx - un.clen);
-        const int64_t rbase = (int64_t)(r - lrow[i]) * rstride;
-        dma((in_ctx ? kc_g : kb_g) + rbase + koff[i], st + q * 512);
-        dma((in_ctx ? vc_g : vb_g) + rbase + voff[i], st + TILE_ELEMS + q * 512);
+        const int64_t r = in_ctx ? (paged ? paged_row(s_pg, kidx, pfirst, np_m1) : (int64_t)ctx0 + kidx)
+                                 : (int64_t)un.blk0 + (kidx - un.clen);
+        const int64_t rbase = (r - lrow[i]) * rstride;
+        // select values, not the pointer variables themselves (a conditional of
+        // the two lvalues would keep them in private memory)
+        const uintptr_t ks = in_ctx ? (uintptr_t)kc_g : (uintptr_t)kb_g;
+        const uintptr_t vs = in_ctx ? (uintptr_t)vc_g : (uintptr_t)vb_g;
+        dma(reinterpret_cast<const bf16*>(ks) + rbase + koff[i], st + q * 512);
+        dma(reinterpret_cast<const bf16*>(vs) + rbase + voff[i], st + TILE_ELEMS + q * 512);
       }
     }
   };
@@ -511,6 +566,22 @@ __global__ __launch_bounds__(NT) void block_attn_bf16_kernel(AttnArgs a) {
   const int32_t qmax = un.clen + un.blen - 1;
   constexpr float TAU = 8.0f;  // rescale only when a row max grows by > 2^8
 
+  if (npg > 0) {
+    // 64 page ids per wave-wide copy (4 bytes a lane); indices past the
+    // table row are clamped into it.
+    const int32_t* bt_r = a.bt + (int64_t)un.r * a.bt_stride;
+    for (int32_t c = w; c * 64 < npg; c += NT / 64) {
+      const int32_t idx = min(pfirst + c * 64 + lane, a.bt_stride - 1);
+      const uint32_t lds_addr =
+          __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)(s_pg + c * 64));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                   :
+                   : "s"(lds_addr), "v"(bt_r + idx)
+                   : "memory", "m0");
+    }
+    wait_vmcnt<0>();
+    block_barrier();
+  }
 #pragma unroll
   for (int t = 0; t < NSTAGE - 1; ++t)
     if (t < ntiles) issue_tile(t);
@@ -809,6 +880,8 @@ struct F32Args {
   int32_t num_reqs, hq, hkv, group;
   float scale;
   int32_t causal, window;
+  const int32_t* bt;  // paged context store (nullptr: packed rows)
+  int32_t bt_stride, num_pages_m1;
 };
 
 template <int DH>
@@ -856,8 +929,15 @@ __global__ __launch_bounds__(64) void block_attn_f32_kernel(F32Args a) {
     const float* vrow_mine = nullptr;
     if (vis) {
       if (kidx < clen) {
-        const int64_t row = (int64_t)c0 + kidx;
-        if (row < a.total_ctx) { krow = a.kc + (row * a.hkv + g) * DH; vrow_mine = a.vc + (row * a.hkv + g) * DH; }
+        int64_t row = (int64_t)c0 + kidx;
+        bool ok = row < a.total_ctx;
+        if (a.bt) {
+          const int32_t pid = min(max(a.bt[(int64_t)r * a.bt_stride + min(kidx / PAGE, a.bt_stride - 1)], 0),
+                                  a.num_pages_m1);
+          row = (int64_t)pid * PAGE + kidx % PAGE;
+          ok = true;
+        }
+        if (ok) { krow = a.kc + (row * a.hkv + g) * DH; vrow_mine = a.vc + (row * a.hkv + g) * DH; }
       } else {
         const int64_t row = (int64_t)b0 + (kidx - clen);
         if (row < a.total_blk) { krow = a.kb + (row * a.hkv + g) * DH; vrow_mine = a.vb + (row * a.hkv + g) * DH; }
@@ -964,14 +1044,22 @@ int32_t host_choose_chunk(const HostReq* rq, int32_t nreq, int32_t units) {
 }
 // Fill hs from the host lengths; false (hs->nreq = 0) when they are absent or
 // the plan does not fit the table.
-bool plan_host_schedule(const dflash_block_attn_params& p, const AttnPlan& plan, HostSched* hs) {
+bool plan_host_schedule(const dflash_block_attn_params& p, const AttnPlan& plan, bool paged,
+                        HostSched* hs) {
   hs->nreq = 0;
   if (!p.host_cu_ctx_lens || !p.host_cu_blk_lens) return false;
   if (p.num_reqs > HS_MAX_REQS || plan.units > INT32_MAX) return false;
   HostReq rq[HS_MAX_REQS];
   for (int32_t r = 0; r < p.num_reqs; ++r) rq[r] = host_req(p, plan.group, r);
   const int32_t units = (int32_t)plan.units;
-  const int32_t chunk = plan.chunk > 0 ? plan.chunk : host_choose_chunk(rq, p.num_reqs, units);
+  // same budgets, in the same order, as choose_chunk on the device
+  int32_t chunk = plan.chunk;
+  if (chunk <= 0) {
+    const int32_t pref = (int32_t)plan.units_pref;
+    chunk = host_choose_chunk(rq, p.num_reqs, pref);
+    if (paged && chunk > PAGED_MAX_UNIT_KEYS && pref < units)
+      chunk = host_choose_chunk(rq, p.num_reqs, units);
+  }
   int32_t ubase = 0;
   // (keys, canonical index, entry) of every unit; sorted by decreasing keys
   std::pair<int32_t, int32_t> key[HS_MAX_UNITS];
@@ -1000,7 +1088,8 @@ bool plan_host_schedule(const dflash_block_attn_params& p, const AttnPlan& plan,
 
 }  // namespace
 
-bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPlan* plan) {
+bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool paged,
+                          AttnPlan* plan) {
   AttnPlan pl{};
   pl.group = p.num_q_heads / p.num_kv_heads;
   const int64_t qt = ((int64_t)pl.group * p.max_blk_len + QROWS - 1) / QROWS;
@@ -1024,6 +1113,13 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPl
     pl.units = (2 * base <= slots_per_head) ? slots_per_head
                                             : std::max(2 * base, 2 * slots_per_head);
   }
+  pl.units_pref = pl.units;
+  if (paged && p.split_keys == 0) {
+    // room for units of at most PAGED_MAX_UNIT_KEYS keys (used only when the
+    // packed budget's split would be longer)
+    const int64_t need = (int64_t)pl.qtiles * ((eff + PAGED_MAX_UNIT_KEYS - 1) / PAGED_MAX_UNIT_KEYS + p.num_reqs);
+    pl.units = std::max(pl.units, need);
+  }
   size_t off = 256;  // reserved header
   pl.off_counters = off;
   off = align_up(off + sizeof(int32_t) * (size_t)p.num_reqs * pl.qtiles * p.num_kv_heads, 256);
@@ -1037,7 +1133,7 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPl
 }
 
 hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnPlan& plan,
-                                  const dflash_qk_prologue* pro,
+                                  const dflash_qk_prologue* pro, const dflash_paged_ctx* pg,
                                   const int32_t* cu_ctx, const int32_t* cu_blk, const void* q,
                                   const void* kb, const void* vb, const void* kc, const void* vc,
                                   void* out, void* ws, hipStream_t s) {
@@ -1049,6 +1145,11 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
     a.total_ctx = p.total_ctx; a.total_blk = p.total_blk;
     a.num_reqs = p.num_reqs; a.hq = p.num_q_heads; a.hkv = p.num_kv_heads;
     a.group = plan.group; a.scale = p.scale; a.causal = p.causal ? 1 : 0; a.window = p.window;
+    if (pg) {
+      a.bt = pg->block_table;
+      a.bt_stride = pg->max_pages_per_req;
+      a.num_pages_m1 = (int32_t)std::min<int64_t>(pg->num_pages - 1, INT32_MAX);
+    }
     const int64_t blocks = p.total_blk * p.num_q_heads;
     if (p.head_dim == 128)
       hipLaunchKernelGGL(block_attn_f32_kernel<128>, dim3((unsigned)blocks), dim3(64), 0, s, a);
@@ -1068,7 +1169,13 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.num_reqs = p.num_reqs; a.hq = p.num_q_heads; a.hkv = p.num_kv_heads;
   a.group = plan.group; a.chunk = plan.chunk; a.qtiles = plan.qtiles;
   a.units = (int32_t)plan.units;
+  a.units_pref = (int32_t)plan.units_pref;
   a.hdr = (int32_t*)w;
+  if (pg) {
+    a.bt = pg->block_table;
+    a.bt_stride = pg->max_pages_per_req;
+    a.num_pages_m1 = (int32_t)std::min<int64_t>(pg->num_pages - 1, INT32_MAX);
+  }
   if (pro) {
     a.qnw = pro->q_norm_w;
     a.knw = pro->k_norm_w;
@@ -1080,11 +1187,11 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.max_blk = p.max_blk_len;
   a.scale_log2 = p.scale * LOG2E;
   a.causal = p.causal ? 1 : 0; a.window = p.window;
-  plan_host_schedule(p, plan, &a.hs);
+  plan_host_schedule(p, plan, pg != nullptr, &a.hs);
   // Host-planned: launch only the units the plan uses.
   const int64_t blocks = (a.hs.nreq > 0 ? a.hs.nunits : plan.units) * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
-  const size_t lds = (size_t)NSTAGE * 2 * KT * p.head_dim * sizeof(bf16);
+  const size_t lds = (size_t)NSTAGE * 2 * KT * p.head_dim * sizeof(bf16) + PG_MAX * sizeof(int32_t);
   // The LDS limit attribute is a per-function setting: raise it once per
   // device (not per launch, so that stream capture sees only the launch).
   static std::once_flag once[64];
@@ -1092,13 +1199,13 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   (void)hipGetDevice(&dev);
   std::call_once(once[dev & 63], [] {
     (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2 + PG_MAX * 4);
     (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2 + PG_MAX * 4);
     (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + PG_MAX * 4);
     (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + PG_MAX * 4);
   });
   const int64_t mblocks = (int64_t)p.num_reqs * plan.qtiles * p.num_kv_heads * (QROWS / MROWS);
   const dim3 grid((unsigned)blocks), blk(NT), mgrid((unsigned)mblocks);

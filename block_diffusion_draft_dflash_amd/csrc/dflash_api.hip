@@ -41,6 +41,7 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // plan (and therefore the workspace size and the bitwise result for a given
 // input) is a pure function of the parameters.
 constexpr int kPlanComputeUnits = 256;
+constexpr int kPagedMaxUnitKeys = 16384;  // keys per work unit over a paged store
 
 dflash_status check_head_geometry(int32_t hq, int32_t hkv, int32_t dh, bool need_q) {
   if (hkv < 1) return fail(DFLASH_ERR_INVALID_ARG, "num_kv_heads must be >= 1 (got %d)", hkv);
@@ -61,7 +62,7 @@ extern "C" {
 
 const char* dflash_last_error(void) { return g_last_error.c_str(); }
 
-int dflash_abi_version(void) { return 101; }
+int dflash_abi_version(void) { return 102; }
 
 dflash_status dflash_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
                                 void* stream) {
@@ -158,9 +159,91 @@ dflash_status dflash_block_attention_check(const dflash_block_attn_params* p) {
 size_t dflash_block_attention_workspace_size(const dflash_block_attn_params* p) {
   if (dflash_block_attention_check(p) != DFLASH_OK) return 0;
   dflash::AttnPlan plan;
-  dflash::plan_block_attention(*p, kPlanComputeUnits, &plan);
+  dflash::plan_block_attention(*p, kPlanComputeUnits, false, &plan);
   return plan.bytes;
 }
+
+size_t dflash_block_attention_paged_workspace_size(const dflash_block_attn_params* p) {
+  if (dflash_block_attention_check(p) != DFLASH_OK) return 0;
+  if (p->split_keys > kPagedMaxUnitKeys) return 0;
+  dflash::AttnPlan plan;
+  dflash::plan_block_attention(*p, kPlanComputeUnits, true, &plan);
+  return plan.bytes;
+}
+
+}  // extern "C"
+
+namespace {
+
+// Shared by the packed and the paged entry points (pg == NULL: packed).
+dflash_status block_attention_impl(const char* who, const dflash_block_attn_params* p,
+                                   const dflash_paged_ctx* pg, const dflash_qk_prologue* prologue,
+                                   const int32_t* cu_ctx_lens, const int32_t* cu_blk_lens,
+                                   const void* q, const void* k_blk, const void* v_blk,
+                                   const void* k_ctx, const void* v_ctx, void* out,
+                                   void* workspace, size_t workspace_bytes, void* stream) {
+  dflash_status st = dflash_block_attention_check(p);
+  if (st != DFLASH_OK) return st;
+  if (pg) {
+    if (pg->page_size != 16)
+      return fail(DFLASH_ERR_UNSUPPORTED, "%s: page_size must be 16 (got %d)", who, pg->page_size);
+    if (pg->max_pages_per_req < 1 || pg->num_pages < 1)
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: max_pages_per_req and num_pages must be >= 1", who);
+    if (p->split_keys > kPagedMaxUnitKeys)
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: split_keys must be <= %d over a paged store", who,
+                  kPagedMaxUnitKeys);
+    if (p->total_blk > 0 && p->total_ctx > 0 && (!pg->block_table || !aligned(pg->block_table, 4)))
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: block_table is NULL or misaligned", who);
+  }
+  if (p->total_blk == 0) return ok();
+  if (!cu_ctx_lens || !cu_blk_lens)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: cu_ctx_lens/cu_blk_lens are NULL", who);
+  if (!q || !k_blk || !v_blk || !out)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: q/k_blk/v_blk/out must not be NULL", who);
+  if (p->total_ctx > 0 && (!k_ctx || !v_ctx))
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: context K/V are NULL but total_ctx > 0", who);
+  const void* tens[] = {q, k_blk, v_blk, out, k_ctx, v_ctx};
+  for (const void* t : tens)
+    if (t && !aligned(t, 16))
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: tensors must be 16-byte aligned", who);
+  dflash::AttnPlan plan;
+  dflash::plan_block_attention(*p, kPlanComputeUnits, pg != nullptr, &plan);
+  if (plan.bytes > 0) {
+    if (!workspace)
+      return fail(DFLASH_ERR_WORKSPACE, "%s: workspace is NULL (%zu bytes needed)", who, plan.bytes);
+    if (!aligned(workspace, 256))
+      return fail(DFLASH_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+    if (workspace_bytes < plan.bytes)
+      return fail(DFLASH_ERR_WORKSPACE, "%s: workspace has %zu bytes, %zu needed", who,
+                  workspace_bytes, plan.bytes);
+  }
+  if (prologue) {
+    if (p->dtype != DFLASH_BF16)
+      return fail(DFLASH_ERR_UNSUPPORTED, "%s: the fused prologue needs bf16", who);
+    if (p->max_blk_len > 64)
+      return fail(DFLASH_ERR_UNSUPPORTED, "%s: the fused prologue needs max_blk_len <= 64 (got %d)",
+                  who, p->max_blk_len);
+    if (!prologue->q_norm_w || !prologue->k_norm_w || !prologue->positions || !prologue->rope_table)
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: NULL pointer in the prologue", who);
+    if (!aligned(prologue->q_norm_w, 16) || !aligned(prologue->k_norm_w, 16) ||
+        !aligned(prologue->rope_table, 16))
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: prologue tensors must be 16-byte aligned", who);
+    if (prologue->max_pos < 1)
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: prologue max_pos must be >= 1", who);
+    if (!(prologue->eps >= 0.f) || !std::isfinite(prologue->eps))
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: prologue eps must be finite and >= 0", who);
+  }
+  if (plan.units * p->num_kv_heads > INT32_MAX)
+    return fail(DFLASH_ERR_UNSUPPORTED, "%s: too many work units", who);
+  return hip_status(dflash::launch_block_attention(*p, plan, prologue, pg, cu_ctx_lens, cu_blk_lens,
+                                                   q, k_blk, v_blk, k_ctx, v_ctx, out, workspace,
+                                                   (hipStream_t)stream),
+                    "block_attention launch");
+}
+
+}  // namespace
+
+extern "C" {
 
 dflash_status dflash_block_attention(const dflash_block_attn_params* p,
                                      const dflash_qk_prologue* prologue, const int32_t* cu_ctx_lens,
@@ -168,54 +251,47 @@ dflash_status dflash_block_attention(const dflash_block_attn_params* p,
                                      const void* v_blk, const void* k_ctx, const void* v_ctx,
                                      void* out, void* workspace, size_t workspace_bytes,
                                      void* stream) {
-  dflash_status st = dflash_block_attention_check(p);
-  if (st != DFLASH_OK) return st;
-  if (p->total_blk == 0) return ok();
-  if (!cu_ctx_lens || !cu_blk_lens)
-    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: cu_ctx_lens/cu_blk_lens are NULL");
-  if (!q || !k_blk || !v_blk || !out)
-    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: q/k_blk/v_blk/out must not be NULL");
-  if (p->total_ctx > 0 && (!k_ctx || !v_ctx))
-    return fail(DFLASH_ERR_INVALID_ARG, "block_attention: k_ctx/v_ctx are NULL but total_ctx > 0");
-  const void* tens[] = {q, k_blk, v_blk, out, k_ctx, v_ctx};
-  for (const void* t : tens)
-    if (t && !aligned(t, 16))
-      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: tensors must be 16-byte aligned");
-  dflash::AttnPlan plan;
-  dflash::plan_block_attention(*p, kPlanComputeUnits, &plan);
-  if (plan.bytes > 0) {
-    if (!workspace)
-      return fail(DFLASH_ERR_WORKSPACE, "block_attention: workspace is NULL (%zu bytes needed)",
-                  plan.bytes);
-    if (!aligned(workspace, 256))
-      return fail(DFLASH_ERR_WORKSPACE, "block_attention: workspace must be 256-byte aligned");
-    if (workspace_bytes < plan.bytes)
-      return fail(DFLASH_ERR_WORKSPACE, "block_attention: workspace has %zu bytes, %zu needed",
-                  workspace_bytes, plan.bytes);
-  }
-  if (prologue) {
-    if (p->dtype != DFLASH_BF16)
-      return fail(DFLASH_ERR_UNSUPPORTED, "block_attention: the fused prologue needs bf16");
-    if (p->max_blk_len > 64)
-      return fail(DFLASH_ERR_UNSUPPORTED,
-                  "block_attention: the fused prologue needs max_blk_len <= 64 (got %d)",
-                  p->max_blk_len);
-    if (!prologue->q_norm_w || !prologue->k_norm_w || !prologue->positions || !prologue->rope_table)
-      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: NULL pointer in the prologue");
-    if (!aligned(prologue->q_norm_w, 16) || !aligned(prologue->k_norm_w, 16) ||
-        !aligned(prologue->rope_table, 16))
-      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: prologue tensors must be 16-byte aligned");
-    if (prologue->max_pos < 1)
-      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: prologue max_pos must be >= 1");
-    if (!(prologue->eps >= 0.f) || !std::isfinite(prologue->eps))
-      return fail(DFLASH_ERR_INVALID_ARG, "block_attention: prologue eps must be finite and >= 0");
-  }
-  if (plan.units * p->num_kv_heads > INT32_MAX)
-    return fail(DFLASH_ERR_UNSUPPORTED, "block_attention: too many work units");
-  return hip_status(dflash::launch_block_attention(*p, plan, prologue, cu_ctx_lens, cu_blk_lens, q, k_blk,
-                                                   v_blk, k_ctx, v_ctx, out, workspace,
-                                                   (hipStream_t)stream),
-                    "block_attention launch");
+  return block_attention_impl("block_attention", p, nullptr, prologue, cu_ctx_lens, cu_blk_lens, q,
+                              k_blk, v_blk, k_ctx, v_ctx, out, workspace, workspace_bytes, stream);
+}
+
+dflash_status dflash_block_attention_paged(const dflash_block_attn_params* p,
+                                           const dflash_paged_ctx* pg,
+                                           const dflash_qk_prologue* prologue,
+                                           const int32_t* cu_ctx_lens,
+                                           const int32_t* cu_blk_lens, const void* q,
+                                           const void* k_blk, const void* v_blk,
+                                           const void* k_pool, const void* v_pool, void* out,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream) {
+  if (!pg) return fail(DFLASH_ERR_INVALID_ARG, "block_attention_paged: pg is NULL");
+  return block_attention_impl("block_attention_paged", p, pg, prologue, cu_ctx_lens, cu_blk_lens,
+                              q, k_blk, v_blk, k_pool, v_pool, out, workspace, workspace_bytes,
+                              stream);
+}
+
+dflash_status dflash_kv_scatter(dflash_dtype dtype, const void* k_src, const void* v_src,
+                                const int32_t* slot_mapping, int64_t T, int32_t num_kv_heads,
+                                int32_t head_dim, void* k_pool, void* v_pool, int64_t num_slots,
+                                void* stream) {
+  if (dtype != DFLASH_F32 && dtype != DFLASH_BF16)
+    return fail(DFLASH_ERR_INVALID_ARG, "kv_scatter: unknown dtype %d", (int)dtype);
+  if (T < 0 || num_slots < 0 || num_kv_heads < 1 || head_dim < 1)
+    return fail(DFLASH_ERR_INVALID_ARG, "kv_scatter: sizes must be non-negative (heads >= 1)");
+  const int64_t row_bytes = (int64_t)num_kv_heads * head_dim * (dtype == DFLASH_BF16 ? 2 : 4);
+  if (row_bytes % 16 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "kv_scatter: a row must be a multiple of 16 bytes");
+  if (T == 0 || num_slots == 0) return ok();
+  if (!k_src || !v_src || !slot_mapping || !k_pool || !v_pool)
+    return fail(DFLASH_ERR_INVALID_ARG, "kv_scatter: NULL pointer argument");
+  if (!aligned(k_src, 16) || !aligned(v_src, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16))
+    return fail(DFLASH_ERR_INVALID_ARG, "kv_scatter: tensors must be 16-byte aligned");
+  if (T > ((int64_t)1 << 40) || num_slots > ((int64_t)1 << 40))
+    return fail(DFLASH_ERR_INVALID_ARG, "kv_scatter: too many rows");
+  return hip_status(dflash::launch_kv_scatter(dtype, k_src, v_src, slot_mapping, T, num_kv_heads,
+                                              head_dim, k_pool, v_pool, num_slots,
+                                              (hipStream_t)stream),
+                    "kv_scatter launch");
 }
 
 size_t dflash_context_kv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_kv_heads,

@@ -22,14 +22,21 @@ struct AttnPlan {
   int32_t qtiles;     // bound on 64-row query tiles per (request, kv-head)
   int32_t chunk;      // keys per work unit (multiple of 64)
   int64_t units;      // bound on work units per kv-head (grid = units * Hkv)
+  int64_t units_pref; // unit budget the split is chosen for first (<= units)
   size_t off_counters, off_part_o, off_part_ml, bytes;
 };
-bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, AttnPlan* plan);
+bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool paged,
+                          AttnPlan* plan);
 
 hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnPlan& plan,
-                                  const dflash_qk_prologue* pro, const int32_t* cu_ctx, const int32_t* cu_blk, const void* q,
+                                  const dflash_qk_prologue* pro, const dflash_paged_ctx* pg,
+                                  const int32_t* cu_ctx, const int32_t* cu_blk, const void* q,
                                   const void* kb, const void* vb, const void* kc, const void* vc,
                                   void* out, void* ws, hipStream_t s);
+
+hipError_t launch_kv_scatter(dflash_dtype dt, const void* k_src, const void* v_src,
+                             const int32_t* slots, int64_t rows, int32_t hkv, int32_t dh,
+                             void* k_pool, void* v_pool, int64_t num_slots, hipStream_t s);
 
 size_t context_kv_workspace_bytes(int64_t rows, int32_t hidden, int32_t hkv, int32_t dh);
 hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* wk,

@@ -44,7 +44,8 @@ def to_host_f64(t: torch.Tensor) -> np.ndarray:
 
 class DevicePath:
     def __init__(self, wl: Workload, device: str = "cuda", split_keys: int = 0,
-                 max_pos: Optional[int] = None, host_lengths: bool = True):
+                 max_pos: Optional[int] = None, host_lengths: bool = True, paged: bool = False,
+                 spare_pages: int = 5):
         self.wl = wl
         self.device = device
         dt = wl.dtype
@@ -99,11 +100,53 @@ class DevicePath:
             split_keys,
             host_cu_ctx_lens=wl.cu_ctx if host_lengths else None,
             host_cu_blk_lens=wl.cu_blk if host_lengths else None)
-        self.ws = B.alloc_workspace(B.dflash_block_attention_workspace_size(self.params), device)
+        self.paged = paged
+        if paged:
+            self._init_paged(spare_pages)
+            self.ws = B.alloc_workspace(
+                B.dflash_block_attention_paged_workspace_size(self.params), device)
+        else:
+            self.ws = B.alloc_workspace(B.dflash_block_attention_workspace_size(self.params), device)
+
+    def _init_paged(self, spare_pages: int) -> None:
+        """A paged store holding the context rows: pages handed out in a seeded
+        random order (so a request's pages are scattered over the pool), spare
+        pages left unused, and every slot filled with NaN first, so a read of a
+        slot the table does not map shows up in the output."""
+        wl = self.wl
+        page = 16
+        npages_r = [(int(c) + page - 1) // page for c in wl.ctx_lens]
+        total = sum(npages_r) + spare_pages
+        perm = np.random.default_rng(4242).permutation(total).astype(np.int32)
+        maxp = max(1, max(npages_r) if npages_r else 1)
+        bt = np.full((wl.num_reqs, maxp), -1, dtype=np.int32)
+        slots = np.empty(wl.total_ctx, dtype=np.int32)
+        nxt = 0
+        for r in range(wl.num_reqs):
+            c0 = int(wl.cu_ctx[r])
+            for pidx in range(npages_r[r]):
+                bt[r, pidx] = perm[nxt]
+                nxt += 1
+            for j in range(int(wl.ctx_lens[r])):
+                slots[c0 + j] = bt[r, j // page] * page + j % page
+        self.num_pages = total
+        self.block_table = torch.from_numpy(bt).to(self.device)
+        self.slot_mapping = torch.from_numpy(slots).to(self.device)
+        dt = self.k_ctx.dtype
+        shape = (total, page, wl.hkv, wl.dh)
+        self.k_pool = torch.full(shape, float("nan"), dtype=dt, device=self.device)
+        self.v_pool = torch.full(shape, float("nan"), dtype=dt, device=self.device)
+        self.pg = B.make_paged_ctx(self.block_table, total, page)
 
     # ---------------------------------------------------------------- context
     def prepare_context(self) -> None:
-        """Produce the normed + rotated context keys (and V for hidden-state input)."""
+        """Produce the normed + rotated context keys (and V for hidden-state input);
+        with a paged store, then scatter them to their pool slots."""
+        self._prepare_packed_context()
+        if self.paged and self.wl.total_ctx:
+            B.dflash_kv_scatter(self.k_ctx, self.v_ctx, self.slot_mapping, self.k_pool, self.v_pool)
+
+    def _prepare_packed_context(self) -> None:
         wl = self.wl
         if self.hidden is not None:
             B.dflash_context_kv(self.hidden, self.hidden_norm_w, self.w_k, self.w_v,
@@ -121,17 +164,25 @@ class DevicePath:
             B.dflash_qk_norm_rope(self.q, self.k_blk, self.q_norm_w, self.k_norm_w,
                                   self.blk_pos, self.wl.eps, self.rope)
 
+    def _attn(self, q, k_blk, prologue) -> None:
+        has_ctx = self.wl.total_ctx > 0
+        if self.paged:
+            B.dflash_block_attention_paged(self.params, self.pg, self.cu_ctx, self.cu_blk, q, k_blk,
+                                           self.v_blk, self.k_pool if has_ctx else None,
+                                           self.v_pool if has_ctx else None, self.out, self.ws,
+                                           prologue=prologue)
+        else:
+            B.dflash_block_attention(self.params, self.cu_ctx, self.cu_blk, q, k_blk, self.v_blk,
+                                     self.k_ctx if has_ctx else None,
+                                     self.v_ctx if has_ctx else None, self.out, self.ws,
+                                     prologue=prologue)
+
     def attention(self) -> None:
-        B.dflash_block_attention(self.params, self.cu_ctx, self.cu_blk, self.q, self.k_blk,
-                                 self.v_blk, self.k_ctx if self.wl.total_ctx else None,
-                                 self.v_ctx if self.wl.total_ctx else None, self.out, self.ws)
+        self._attn(self.q, self.k_blk, None)
 
     def attention_fused(self) -> None:
         """Block attention with the q/k norm + RoPE fused in (raw q and k_blk)."""
-        B.dflash_block_attention(self.params, self.cu_ctx, self.cu_blk, self.q_raw, self.k_blk_raw,
-                                 self.v_blk, self.k_ctx if self.wl.total_ctx else None,
-                                 self.v_ctx if self.wl.total_ctx else None, self.out, self.ws,
-                                 prologue=self.prologue)
+        self._attn(self.q_raw, self.k_blk_raw, self.prologue)
 
     def step(self) -> None:
         """One pass of the hot path over the batch: q/k norm + RoPE, block attention

@@ -204,6 +204,67 @@ dflash_status dflash_block_attention(const dflash_block_attn_params* p,
                                      void* stream);
 
 /*
+ * Paged context store ("qwen3_dflash.cpp" page, the fixed-capacity paged
+ * draft-KV store read by the paged block attention in ForwardPagedBody): a
+ * pool [num_pages, page_size, Hkv, Dh] per tensor (K and V), and per request
+ * a row of block_table listing the pages of its context rows in order:
+ * context row k of request r lives at pool page block_table[r * stride +
+ * k / page_size], row k % page_size. Page indices past the table row and page
+ * ids outside [0, num_pages) are clamped into range (wrong values, never an
+ * out-of-bounds access).
+ */
+typedef struct {
+  const int32_t* block_table;  /* device int32 [num_reqs][max_pages_per_req] */
+  int32_t max_pages_per_req;   /* row stride of block_table, >= 1 */
+  int32_t page_size;           /* rows per page; 16 */
+  int64_t num_pages;           /* pages in each pool, >= 1 */
+} dflash_paged_ctx;
+
+/*
+ * dflash_block_attention_paged -- dflash_block_attention with the context
+ * K/V read from a paged store instead of packed rows.
+ *
+ * Identical semantics, arguments and workspace to dflash_block_attention
+ * except: k_pool / v_pool are [num_pages, 16, Hkv, Dh] pools addressed through
+ * pg->block_table; cu_ctx_lens still gives each request's context length
+ * (C_r = cu_ctx_lens[r+1] - cu_ctx_lens[r], the pages' seq_lens) and
+ * p->total_ctx = cu_ctx_lens[R]. The work split is the packed call's for the
+ * same lengths whenever that split has at most 16384 keys per work unit (then
+ * the result is bitwise the packed call's); longer splits are cut to that
+ * size (split_keys, if given, must not exceed it). Requires page_size == 16
+ * (DFLASH_ERR_UNSUPPORTED otherwise). The workspace is sized by
+ * dflash_block_attention_paged_workspace_size (>= the packed size).
+ */
+dflash_status dflash_block_attention_paged(const dflash_block_attn_params* p,
+                                           const dflash_paged_ctx* pg,
+                                           const dflash_qk_prologue* prologue,
+                                           const int32_t* cu_ctx_lens,
+                                           const int32_t* cu_blk_lens, const void* q,
+                                           const void* k_blk, const void* v_blk,
+                                           const void* k_pool, const void* v_pool, void* out,
+                                           void* workspace, size_t workspace_bytes,
+                                           void* stream);
+
+/* Bytes of workspace dflash_block_attention_paged needs (0 if invalid). */
+size_t dflash_block_attention_paged_workspace_size(const dflash_block_attn_params* p);
+
+/*
+ * dflash_kv_scatter -- append rows to a paged store: for every row t with
+ * 0 <= slot_mapping[t] < num_slots, pool row slot_mapping[t] of k_pool and
+ * v_pool (a flat view [num_slots, Hkv, Dh], slot = page * page_size + offset)
+ * receives row t of k_src and v_src; other rows (e.g. the padding slot -1)
+ * are skipped. The pages' store appends context rows this way (an index copy
+ * to slots). Rows with equal slots race (the caller gives distinct slots).
+ *
+ *   dtype        of every tensor; k_src, v_src [T, Hkv, Dh]; slot_mapping int32 [T].
+ *   T may be 0 (nothing is enqueued).
+ */
+dflash_status dflash_kv_scatter(dflash_dtype dtype, const void* k_src, const void* v_src,
+                                const int32_t* slot_mapping, int64_t T, int32_t num_kv_heads,
+                                int32_t head_dim, void* k_pool, void* v_pool, int64_t num_slots,
+                                void* stream);
+
+/*
  * dflash_context_kv -- context K/V precompute (bf16).
  *
  * For each context row t: n = RMSNorm(hidden[t], hidden_norm_w); K = n W_k^T,

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_error_string(lib):
-    assert lib.dflash_abi_version() == 101
+    assert lib.dflash_abi_version() == 102
     assert isinstance(lib.dflash_last_error(), bytes)
 
 
@@ -132,6 +132,37 @@ def test_host_lengths_shape_errors(lib):
     q = P()
     q.host_cu_ctx_lens = ctypes.cast(p._host_lens[0], ctypes.c_void_p)
     assert B.dflash_block_attention_check(q) == B.DFLASH_ERR_INVALID_ARG
+
+
+def _paged_call(lib, p, pg):
+    # validation happens before any pointer is touched; NULL device pointers
+    return lib.dflash_block_attention_paged(ctypes.byref(p), ctypes.byref(pg) if pg else None,
+                                            None, None, None, None, None, None, None, None, None,
+                                            None, 0, None)
+
+
+def test_paged_validation(lib):
+    pg = B.PagedCtx(None, 64, 16, 1000)
+    assert _paged_call(lib, P(), None) == B.DFLASH_ERR_INVALID_ARG
+    assert _paged_call(lib, P(), B.PagedCtx(None, 64, 8, 1000)) == B.DFLASH_ERR_UNSUPPORTED
+    assert _paged_call(lib, P(), B.PagedCtx(None, 64, 16, 0)) == B.DFLASH_ERR_INVALID_ARG
+    assert _paged_call(lib, P(), B.PagedCtx(None, 0, 16, 10)) == B.DFLASH_ERR_INVALID_ARG
+    assert _paged_call(lib, P(split_keys=32768), pg) == B.DFLASH_ERR_INVALID_ARG
+    assert _paged_call(lib, P(), pg) == B.DFLASH_ERR_INVALID_ARG  # block_table NULL
+    assert _paged_call(lib, P(total_blk=0, max_blk_len=0), pg) == B.DFLASH_OK  # nothing to do
+    # the paged workspace holds at least the packed one; a split past the paged cap has none
+    assert B.dflash_block_attention_paged_workspace_size(P()) >= \
+        B.dflash_block_attention_workspace_size(P())
+    assert B.dflash_block_attention_paged_workspace_size(P(split_keys=32768)) == 0
+
+
+def test_kv_scatter_validation(lib):
+    f = lib.dflash_kv_scatter
+    assert f(7, None, None, None, 4, 8, 128, None, None, 64, None) == B.DFLASH_ERR_INVALID_ARG
+    assert f(B.DFLASH_BF16, None, None, None, 4, 1, 2, None, None, 64, None) == B.DFLASH_ERR_UNSUPPORTED
+    assert f(B.DFLASH_BF16, None, None, None, 0, 8, 128, None, None, 64, None) == B.DFLASH_OK
+    assert f(B.DFLASH_BF16, None, None, None, 4, 8, 128, None, None, 64, None) == B.DFLASH_ERR_INVALID_ARG
+    assert f(B.DFLASH_BF16, None, None, None, -1, 8, 128, None, None, 64, None) == B.DFLASH_ERR_INVALID_ARG
 
 
 def test_workspace_sizes(lib):
