@@ -15,4 +15,5 @@ from .dflash_oracle import (  # noqa: F401
     attention_visibility,
     block_attention,
     draft_block_attention,
+    paged_context_rows,
 )

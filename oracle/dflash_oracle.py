@@ -20,6 +20,10 @@ Sources (pages of the vllm.cpp project):
     [context; block] sequence, only block-query rows kept).
   * "qwen3.cpp" page -- file header (standard, non-gemma RMSNorm; q/k norm
     applied before RoPE).
+  * "qwen3_dflash.cpp" page, the paged draft-KV store read by
+    ``ForwardPagedBody``: pools of fixed-size pages, a per-request block table
+    of page ids; context row p of a request lives at page p // page_size,
+    offset p % page_size.
 
 Readings taken where the pages are silent (each also listed in the design doc):
   * GQA: q-head h reads kv-head h // (Hq/Hkv).
@@ -52,6 +56,7 @@ __all__ = [
     "attention_visibility",
     "block_attention",
     "draft_block_attention",
+    "paged_context_rows",
 ]
 
 
@@ -238,3 +243,19 @@ def draft_block_attention(q, k_blk, v_blk, blk_positions, k_ctx_hat, v_ctx,
     out = block_attention(q_hat, k_hat, v_blk, k_ctx_hat, v_ctx, cu_ctx, cu_blk,
                           scale, causal, window)
     return out, q_hat, k_hat
+
+
+def paged_context_rows(pool, block_table, ctx_lens, page_size=16):
+    """The packed context rows a paged store holds: for request r and context
+    row k < ctx_lens[r], row pool[block_table[r][k // page_size], k % page_size]
+    ("qwen3_dflash.cpp" page, the paged draft-KV store). ``pool`` is
+    [pages, page_size, ...]; requests are concatenated in order."""
+    pool = np.asarray(pool)
+    block_table = np.asarray(block_table)
+    rows = []
+    for r, c in enumerate(np.asarray(ctx_lens).tolist()):
+        for k in range(int(c)):
+            rows.append(pool[int(block_table[r][k // page_size]), k % page_size])
+    if not rows:
+        return np.zeros((0,) + pool.shape[2:], dtype=pool.dtype)
+    return np.stack(rows)

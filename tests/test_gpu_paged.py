@@ -128,3 +128,28 @@ def test_paged_unit_cap(dflash):
     print(f"[paged unit cap] max abs diff {d.max().item():.3e} mean {d.mean().item():.3e}")
     assert not torch.isnan(out_paged.float()).any()
     assert d.max().item() <= 2e-2 and d.mean().item() <= 2e-3
+
+
+@pytest.mark.parametrize("case", ["swa_unaligned_window", "empty_ctx_and_blocks"])
+def test_paged_vs_oracle_through_the_pools(case):
+    # the oracle reads the context rows out of the device pools by the paged
+    # layout's definition and computes the attention on them
+    from block_diffusion_draft_dflash_amd.pipeline import to_host_f64
+    from oracle import dflash_oracle as O
+    print(f"case paged oracle {case}", flush=True)
+    kw = dict(CASES[case])
+    name = kw.pop("name")
+    wl = make_workload(name, **kw)
+    dp = DevicePath(wl, paged=True)
+    dp.prepare_context()
+    dp.step_fused()
+    torch.cuda.synchronize()
+    bt = dp.block_table.cpu().numpy()
+    k_ctx = O.paged_context_rows(to_host_f64(dp.k_pool), bt, wl.ctx_lens)
+    v_ctx = O.paged_context_rows(to_host_f64(dp.v_pool), bt, wl.ctx_lens)
+    ref, _, _ = O.draft_block_attention(wl.q, wl.k_blk, wl.v_blk, wl.blk_positions, k_ctx, v_ctx,
+                                        wl.cu_ctx, wl.cu_blk, wl.q_norm_w, wl.k_norm_w, wl.eps,
+                                        wl.theta, wl.scale, wl.causal, wl.window)
+    err = np.abs(to_host_f64(dp.out) - ref)
+    print(f"[paged oracle {case}] max abs {err.max():.3e} mean abs {err.mean():.3e}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3

@@ -499,5 +499,58 @@ def _compose_ckv(ns, h, wn, wk, wv, wkn, pos, hkv, d, eps, theta):
 
 def test_oracle_package_exports():
     for name in ("rms_norm", "rope_neox", "qk_norm_rope", "context_kv", "block_attention",
-                 "draft_block_attention"):
+                 "draft_block_attention", "paged_context_rows"):
         assert callable(getattr(oracle, name))
+
+
+# ---------------------------------------------------------------- paged context store
+
+def _paged_fixture(seed=5, page=16):
+    rng = np.random.default_rng(seed)
+    ctx_lens = np.array([0, 1, 15, 16, 17, 40], dtype=np.int64)
+    rows = rng.standard_normal((int(ctx_lens.sum()), 3, 4))
+    npages = [(int(c) + page - 1) // page for c in ctx_lens]
+    total = sum(npages) + 3
+    perm = rng.permutation(total)
+    bt = np.full((len(ctx_lens), max(npages)), -1, dtype=np.int64)
+    nxt = 0
+    slots = []
+    for r, c in enumerate(ctx_lens.tolist()):
+        for p_ in range(npages[r]):
+            bt[r, p_] = perm[nxt]
+            nxt += 1
+        slots += [bt[r, k // page] * page + k % page for k in range(c)]
+    pool = np.full((total * page, 3, 4), np.nan)
+    pool[np.array(slots, dtype=np.int64)] = rows       # flat-slot scatter, written independently
+    return pool.reshape(total, page, 3, 4), bt, ctx_lens, rows
+
+
+def test_paged_rows_round_trip():
+    # rows scattered to flat slots (page * 16 + offset) come back in order
+    pool, bt, lens, rows = _paged_fixture()
+    got = O.paged_context_rows(pool, bt, lens)
+    assert got.shape == rows.shape and np.array_equal(got, rows)
+
+
+def test_paged_rows_identity_table():
+    # the pages' own store: one request, identity table, row p at flat slot p
+    rng = np.random.default_rng(9)
+    flat = rng.standard_normal((5 * 16, 2, 3))
+    got = O.paged_context_rows(flat.reshape(5, 16, 2, 3), np.arange(5)[None, :], [70])
+    assert np.array_equal(got, flat[:70])
+
+
+def test_paged_rows_pin_catches_index_mistakes():
+    pool, bt, lens, rows = _paged_fixture()
+
+    def wrong_offset(pool, bt, lens, page=16):  # offset taken from the wrong end of the page
+        return np.stack([pool[int(bt[r][k // page]), page - 1 - k % page]
+                         for r, c in enumerate(lens) for k in range(int(c))])
+
+    def wrong_page(pool, bt, lens, page=16):  # pages counted from 1
+        return np.stack([pool[int(bt[r][min(k // page + 1, bt.shape[1] - 1)]), k % page]
+                         for r, c in enumerate(lens) for k in range(int(c))])
+
+    for f in (wrong_offset, wrong_page):
+        got = f(pool, bt, lens)
+        assert not np.array_equal(got, rows)
