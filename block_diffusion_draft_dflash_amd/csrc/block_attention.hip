@@ -42,6 +42,7 @@ constexpr int QROWS = 64;  // query rows per work unit
 constexpr int PAGE = 16;   // rows per page of the paged context store
 constexpr int PAGED_MAX_UNIT_KEYS = 16384;             // keys per unit over a paged store
 constexpr int PG_MAX = PAGED_MAX_UNIT_KEYS / PAGE + 64;  // page ids a unit stages in LDS
+constexpr int POS_LDS = 4 * 64;  // block positions staged by the fused prologue (64 per wave)
 constexpr int KT = 32;     // keys per tile
 constexpr int NT = 256;    // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
@@ -309,10 +310,46 @@ constexpr int NSTAGE = 4;  // LDS stages: NSTAGE - 1 tiles in flight
 // j + 4 ds (ds < DS) of 8 elements, i.e. d = 8 (j + 4 ds) + e; chunk ds pairs
 // with chunk ds + DS/2 (d and d + Dh/2). Same arithmetic as qk_norm_rope_kernel:
 // y = x * (1/rms) * w, then (y_lo c - y_hi s, y_hi c + y_lo s), rounded once.
+// The operands (weights of the lane's dims, cos/sin of its pairs at the row's
+// position) are loaded apart from the arithmetic, so that the kernel can
+// issue those loads while its first tile copies are in flight.
 template <int DH>
-__device__ __forceinline__ void norm_rope_frag(const bf16x8 (&xin)[DH / 32], const float* w,
-                                               const float2* cs, float eps, int j,
-                                               bf16x8 (&out)[DH / 32]) {
+struct RopeOps {
+  float wlo[DH / 64][8], whi[DH / 64][8], c[DH / 64][8], sn[DH / 64][8];
+};
+
+template <int DH>
+__device__ __forceinline__ void load_rope_weights(const float* w, int j, RopeOps<DH>& o) {
+#pragma unroll
+  for (int ds = 0; ds < DH / 64; ++ds) {
+    const int dlo = 8 * (j + 4 * ds);
+    const float4* wl = reinterpret_cast<const float4*>(w + dlo);
+    const float4* wh = reinterpret_cast<const float4*>(w + dlo + DH / 2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const float4 l = wl[h], u = wh[h];
+      o.wlo[ds][4 * h] = l.x; o.wlo[ds][4 * h + 1] = l.y; o.wlo[ds][4 * h + 2] = l.z; o.wlo[ds][4 * h + 3] = l.w;
+      o.whi[ds][4 * h] = u.x; o.whi[ds][4 * h + 1] = u.y; o.whi[ds][4 * h + 2] = u.z; o.whi[ds][4 * h + 3] = u.w;
+    }
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ void load_rope_cs(const float2* cs, int j, RopeOps<DH>& o) {
+#pragma unroll
+  for (int ds = 0; ds < DH / 64; ++ds) {
+    const float4* c4 = reinterpret_cast<const float4*>(cs + 8 * (j + 4 * ds));
+#pragma unroll
+    for (int h = 0; h < 4; ++h) {
+      const float4 v = c4[h];
+      o.c[ds][2 * h] = v.x; o.sn[ds][2 * h] = v.y; o.c[ds][2 * h + 1] = v.z; o.sn[ds][2 * h + 1] = v.w;
+    }
+  }
+}
+
+template <int DH>
+__device__ __forceinline__ void apply_norm_rope(const bf16x8 (&xin)[DH / 32], const RopeOps<DH>& o,
+                                                float eps, bf16x8 (&out)[DH / 32]) {
   constexpr int DS = DH / 32;
   float x[DS][8];
   float ss = 0.f;
@@ -326,28 +363,14 @@ __device__ __forceinline__ void norm_rope_frag(const bf16x8 (&xin)[DH / 32], con
   ss = xrow4_sum(ss);
   const float inv = 1.0f / sqrtf(ss * (1.0f / DH) + eps);
 #pragma unroll
-  for (int ds = 0; ds < DS / 2; ++ds) {
-    const int dlo = 8 * (j + 4 * ds);
-    const float4* wl = reinterpret_cast<const float4*>(w + dlo);
-    const float4* wh = reinterpret_cast<const float4*>(w + dlo + DH / 2);
-    const float4* c4 = reinterpret_cast<const float4*>(cs + dlo);
-    const float4 wl0 = wl[0], wl1 = wl[1], wh0 = wh[0], wh1 = wh[1];
-    const float wlo[8] = {wl0.x, wl0.y, wl0.z, wl0.w, wl1.x, wl1.y, wl1.z, wl1.w};
-    const float whi[8] = {wh0.x, wh0.y, wh0.z, wh0.w, wh1.x, wh1.y, wh1.z, wh1.w};
-    float c[8], sn[8];
-#pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      const float4 v = c4[h];
-      c[2 * h] = v.x; sn[2 * h] = v.y; c[2 * h + 1] = v.z; sn[2 * h + 1] = v.w;
-    }
+  for (int ds = 0; ds < DS / 2; ++ds)
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float lo = x[ds][e] * inv * wlo[e];
-      const float hi = x[ds + DS / 2][e] * inv * whi[e];
-      out[ds][e] = f2bf(lo * c[e] - hi * sn[e]);
-      out[ds + DS / 2][e] = f2bf(hi * c[e] + lo * sn[e]);
+      const float lo = x[ds][e] * inv * o.wlo[ds][e];
+      const float hi = x[ds + DS / 2][e] * inv * o.whi[ds][e];
+      out[ds][e] = f2bf(lo * o.c[ds][e] - hi * o.sn[ds][e]);
+      out[ds + DS / 2][e] = f2bf(hi * o.c[ds][e] + lo * o.sn[ds][e]);
     }
-  }
 }
 
 // Pool row of context key k of a unit over a paged store, from the page ids
@@ -445,14 +468,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     return k_begin + t * KT;
   };
 
-  // Positions needed by the fused prologue: this lane's query row and the
-  // block K row (16 w + m) it normalises.
+  // Block rows of the fused prologue: this lane's query row b and the block
+  // K row (16 w + m) it normalises, as indices into the unit's block rows.
   const int32_t krho = 16 * w + m;
-  int32_t pos_q = 0, pos_k = 0;
-  if constexpr (FUSE) {
-    if (rvalid) pos_q = clamp_pos(a.bpos[qrow], a.max_pos);
-    if (krho < nblk) pos_k = clamp_pos(a.bpos[(int64_t)un.blk0 + (kb_first - un.clen) + krho], a.max_pos);
-  }
+  const int32_t kb_row = (kb_first - un.clen) + krho;
 
   bf16x8 qf[DS];
 #pragma unroll
@@ -489,6 +508,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   // row s_pg[k / PAGE - pfirst] * PAGE + k % PAGE.
   const bool paged = a.bt != nullptr;
   int32_t* const s_pg = reinterpret_cast<int32_t*>(smem + NSTAGE * STAGE_ELEMS);
+  // Fused prologue: each wave's own copy of the positions of the unit's block
+  // rows (lane i: block row i; the prologue requires at most 64 of them).
+  int32_t* const s_pos = s_pg + PG_MAX + 64 * w;
   const int32_t kc_end = min(k_end, un.clen);
   const int32_t pfirst = k_begin / PAGE;
   const int32_t npg = (paged && kc_end > k_begin) ? (kc_end - 1) / PAGE - pfirst + 1 : 0;
@@ -582,18 +604,83 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     wait_vmcnt<0>();
     block_barrier();
   }
+  // Operands of the fused prologue. Every row needs the norm weights and the
+  // cos/sin of its position, and the unit's q rows (G heads) and block K rows
+  // share the positions of its block rows. When they fit, the weights and the
+  // cos/sin rows of the unit's block rows are copied once into the stage that
+  // no tile occupies before the loop, [q weights | k weights | rows], and
+  // every lane reads its operands from LDS; otherwise each lane loads its
+  // own from global memory (per-lane loads of shared data would cost more
+  // vector-memory return bandwidth than the unit's K/V tiles).
+  float* const s_op = reinterpret_cast<float*>(smem + (NSTAGE - 1) * STAGE_ELEMS);
+  float2* const s_cs = reinterpret_cast<float2*>(s_op + 256);
+  constexpr int CPR = DH / 4;    // 16-byte chunks per cos/sin row
+  constexpr int RPD = 64 / CPR;  // cos/sin rows per wave-wide copy (1 KB)
+  const int32_t ncopy = (un.blen + RPD - 1) / RPD;
+  const bool op_lds = FUSE && un.blen > 0 && 1024 * (1 + ncopy) <= STAGE_ELEMS * (int)sizeof(bf16);
+  if constexpr (FUSE) {
+    // The positions travel like the tiles (a direct copy into LDS, waited on
+    // explicitly), ahead of them, so that reading them waits for this copy
+    // only and not for the tiles behind it.
+    const int64_t pidx = max((int64_t)0, min((int64_t)un.blk0 + lane, a.total_blk - 1));
+    const uint32_t lds_addr = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)s_pos);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dword %1, off"
+                 :
+                 : "s"(lds_addr), "v"(a.bpos + pidx)
+                 : "memory", "m0");
+    if (op_lds && w == 0) {
+      // lane l: 16 bytes of the q weights (l < DH / 4), else of the k weights
+      const int which = min(lane / CPR, 1);
+      const float* src = (which == 0 ? a.qnw : a.knw) + (lane % CPR) * 4;
+      const uint32_t lds_w = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)s_op);
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :
+                   : "s"(lds_w), "v"(src)
+                   : "memory", "m0");
+    }
+  }
+  const int32_t nfirst = min(ntiles, NSTAGE - 1);
 #pragma unroll
   for (int t = 0; t < NSTAGE - 1; ++t)
     if (t < ntiles) issue_tile(t);
-  // Settle the q fragments (and the prologue copies) once, before the loop;
-  // inside it the only vector-memory operations are the tile copies.
+  if (FUSE && op_lds) {
+    // positions landed (the tile copies issued after them may stay in
+    // flight); then the cos/sin rows of the block rows, by position
+    if (nfirst >= 3) wait_vmcnt<3 * LPT>();
+    else if (nfirst == 2) wait_vmcnt<2 * LPT>();
+    else if (nfirst == 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+    for (int32_t c = w; c < ncopy; c += NT / 64) {
+      const int32_t row = min(c * RPD + lane / CPR, un.blen - 1);
+      const int32_t pos = clamp_pos(s_pos[min(row, 63)], a.max_pos);
+      const float2* src = a.rope + (int64_t)pos * (DH / 2) + (lane % CPR) * 2;
+      const uint32_t lds_cs =
+          __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)(s_cs + c * RPD * (DH / 2)));
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :
+                   : "s"(lds_cs), "v"(src)
+                   : "memory", "m0");
+    }
+  }
+  // Settle q, the prologue operands and the first copies once, before the
+  // loop; inside it the only vector-memory operations are the tile copies.
   wait_vmcnt<0>();
 
   if constexpr (FUSE) {
+    if (op_lds) block_barrier();  // every wave's operand copies are in LDS
+    RopeOps<DH> ops;              // q's operands, then the block K row's
     // q: RMSNorm + RoPE in registers (rows of this lane group).
-    const float2* csq = a.rope + (int64_t)pos_q * (DH / 2);
+    if (op_lds) {
+      load_rope_weights<DH>(s_op, j, ops);
+      load_rope_cs<DH>(s_cs + min(max(b, 0), un.blen - 1) * (DH / 2), j, ops);
+    } else {
+      const int32_t pos_q = rvalid ? s_pos[min(b, 63)] : 0;
+      load_rope_weights<DH>(a.qnw, j, ops);
+      load_rope_cs<DH>(a.rope + (int64_t)clamp_pos(pos_q, a.max_pos) * (DH / 2), j, ops);
+    }
     bf16x8 qn[DS];
-    norm_rope_frag<DH>(qf, a.qnw, csq, a.eps, j, qn);
+    apply_norm_rope<DH>(qf, ops, a.eps, qn);
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[ds] = rvalid ? qn[ds] : bf16x8{};
     // block K rows: in place in the LDS stages of the first tiles (at most
@@ -610,8 +697,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 #pragma unroll
       for (int ds = 0; ds < DS; ++ds)
         kx[ds] = kv ? *reinterpret_cast<const bf16x8*>(kr + swz_k<DH>(row, j + 4 * ds) * 8) : bf16x8{};
-      const float2* csk = a.rope + (int64_t)pos_k * (DH / 2);
-      norm_rope_frag<DH>(kx, a.knw, csk, a.eps, j, ky);
+      if (op_lds) {
+        load_rope_weights<DH>(s_op + DH, j, ops);
+        load_rope_cs<DH>(s_cs + min(max(kb_row, 0), un.blen - 1) * (DH / 2), j, ops);
+      } else {
+        const int32_t pos_k = kv ? s_pos[min(kb_row, 63)] : 0;
+        load_rope_weights<DH>(a.knw, j, ops);
+        load_rope_cs<DH>(a.rope + (int64_t)clamp_pos(pos_k, a.max_pos) * (DH / 2), j, ops);
+      }
+      apply_norm_rope<DH>(kx, ops, a.eps, ky);
       if (kv) {
 #pragma unroll
         for (int ds = 0; ds < DS; ++ds)
@@ -1105,13 +1199,19 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool p
   } else {
     // The device picks the split size (choose_chunk) so that the units fill
     // the launched grid. Resident workgroup slots: two per compute unit at
-    // this kernel's LDS use. With few (request, query tile) pairs the grid is
-    // one round of slots; with many, two units per pair or two rounds.
+    // this kernel's LDS use. With few (request, query tile) pairs, one unit
+    // per compute unit: fewer, longer splits write fewer partials for the
+    // merge and spread each unit's start-up over more tiles, which measured
+    // faster than filling both slots. With more pairs, one round of slots,
+    // then two units per pair or two rounds.
     pl.chunk = 0;
-    const int64_t slots_per_head = std::max<int64_t>(1, 2LL * (num_cus > 0 ? num_cus : 256) / p.num_kv_heads);
+    const int64_t cus = num_cus > 0 ? num_cus : 256;
+    const int64_t per_cu = std::max<int64_t>(1, cus / p.num_kv_heads);
+    const int64_t slots_per_head = std::max<int64_t>(1, 2 * cus / p.num_kv_heads);
     const int64_t base = (int64_t)p.num_reqs * pl.qtiles;
-    pl.units = (2 * base <= slots_per_head) ? slots_per_head
-                                            : std::max(2 * base, 2 * slots_per_head);
+    pl.units = (2 * base <= per_cu)           ? per_cu
+               : (2 * base <= slots_per_head) ? slots_per_head
+                                              : std::max(2 * base, 2 * slots_per_head);
   }
   pl.units_pref = pl.units;
   if (paged && p.split_keys == 0) {
@@ -1191,7 +1291,7 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   // Host-planned: launch only the units the plan uses.
   const int64_t blocks = (a.hs.nreq > 0 ? a.hs.nunits : plan.units) * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
-  const size_t lds = (size_t)NSTAGE * 2 * KT * p.head_dim * sizeof(bf16) + PG_MAX * sizeof(int32_t);
+  const size_t lds = (size_t)NSTAGE * 2 * KT * p.head_dim * sizeof(bf16) + (PG_MAX + POS_LDS) * sizeof(int32_t);
   // The LDS limit attribute is a per-function setting: raise it once per
   // device (not per launch, so that stream capture sees only the launch).
   static std::once_flag once[64];
@@ -1199,13 +1299,13 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   (void)hipGetDevice(&dev);
   std::call_once(once[dev & 63], [] {
     (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2 + PG_MAX * 4);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2 + (PG_MAX + POS_LDS) * 4);
     (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2 + PG_MAX * 4);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2 + (PG_MAX + POS_LDS) * 4);
     (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + PG_MAX * 4);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + (PG_MAX + POS_LDS) * 4);
     (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + PG_MAX * 4);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + (PG_MAX + POS_LDS) * 4);
   });
   const int64_t mblocks = (int64_t)p.num_reqs * plan.qtiles * p.num_kv_heads * (QROWS / MROWS);
   const dim3 grid((unsigned)blocks), blk(NT), mgrid((unsigned)mblocks);

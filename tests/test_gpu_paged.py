@@ -91,9 +91,10 @@ def test_kv_scatter(dflash):
 
 
 def test_paged_unit_cap(dflash):
-    # With 64 kv-heads the grid holds 8 units per head, so one request of
-    # 140000 context rows gets 17504-key splits in the packed call; over a
-    # paged store units are capped at 16384 keys (more units, other rounding).
+    # With 64 kv-heads and one request the packed call plans 4 units per
+    # head (one per compute unit), so the 140000 context rows go in splits of
+    # about 35000 keys; over a paged store units are capped at 16384 keys
+    # (more units, other rounding).
     print("case paged unit cap", flush=True)
     torch.manual_seed(11)
     hq = hkv = 64
