@@ -305,6 +305,21 @@ __device__ __forceinline__ void block_barrier() {
 
 constexpr int NSTAGE = 4;  // LDS stages: NSTAGE - 1 tiles in flight
 
+// s_waitcnt takes an immediate: wait until at most k * STEP vector-memory
+// operations are outstanding, for a run-time k (clamped to [0, MAXK]).
+template <int STEP, int MAXK>
+__device__ __forceinline__ void wait_vmcnt_steps(int32_t k) {
+  if constexpr (MAXK > 0) {
+    if (k >= MAXK) {
+      wait_vmcnt<MAXK * STEP>();
+      return;
+    }
+    wait_vmcnt_steps<STEP, MAXK - 1>(k);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+
 // Per-head RMSNorm + NeoX RoPE of one head vector held by the four lanes
 // {m, m+16, m+32, m+48} in the MFMA operand layout: this lane holds chunks
 // j + 4 ds (ds < DS) of 8 elements, i.e. d = 8 (j + 4 ds) + e; chunk ds pairs
@@ -646,10 +661,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   if (FUSE && op_lds) {
     // positions landed (the tile copies issued after them may stay in
     // flight); then the cos/sin rows of the block rows, by position
-    if (nfirst >= 3) wait_vmcnt<3 * LPT>();
-    else if (nfirst == 2) wait_vmcnt<2 * LPT>();
-    else if (nfirst == 1) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
+    wait_vmcnt_steps<LPT, NSTAGE - 1>(nfirst);
     asm volatile("" ::: "memory");
     for (int32_t c = w; c < ncopy; c += NT / 64) {
       const int32_t row = min(c * RPD + lane / CPR, un.blen - 1);
@@ -720,10 +732,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   for (int32_t it = 0; it < ntiles; ++it) {
     // Own loads of tile `it` landed (tiles issued after it may stay in flight),
     // then the barrier makes every wave's part visible and frees stage it-1.
-    const int32_t after = min(ntiles - 1 - it, NSTAGE - 2);
-    if (after >= 2) wait_vmcnt<2 * LPT>();
-    else if (after == 1) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
+    wait_vmcnt_steps<LPT, NSTAGE - 2>(ntiles - 1 - it);
     wait_lgkm0();
     block_barrier();
     if (it + NSTAGE - 1 < ntiles) issue_tile(it + NSTAGE - 1);
