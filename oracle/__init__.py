@@ -16,4 +16,8 @@ from .dflash_oracle import (  # noqa: F401
     block_attention,
     draft_block_attention,
     paged_context_rows,
+    residual_rms_norm,
+    block_qkv,
+    output_projection,
+    draft_layer_attention,
 )

@@ -24,6 +24,10 @@ Sources (pages of the vllm.cpp project):
     ``ForwardPagedBody``: pools of fixed-size pages, a per-request block table
     of page ids; context row p of a request lives at page p // page_size,
     offset p % page_size.
+  * "qwen3_dflash.cpp" page, ``ForwardBlockLogits`` and ``ForwardWithCtxKVDev``
+    (the layer around the attention): input_layernorm as the standard
+    residual add + RMSNorm, the merged qkv weight applied as one product and
+    split into q | k | v, and o_proj applied to the attention output.
 
 Readings taken where the pages are silent (each also listed in the design doc):
   * GQA: q-head h reads kv-head h // (Hq/Hkv).
@@ -57,6 +61,10 @@ __all__ = [
     "block_attention",
     "draft_block_attention",
     "paged_context_rows",
+    "residual_rms_norm",
+    "block_qkv",
+    "output_projection",
+    "draft_layer_attention",
 ]
 
 
@@ -259,3 +267,68 @@ def paged_context_rows(pool, block_table, ctx_lens, page_size=16):
     if not rows:
         return np.zeros((0,) + pool.shape[2:], dtype=pool.dtype)
     return np.stack(rows)
+
+
+def residual_rms_norm(hidden, residual, w, eps):
+    """The layer's input norm: ``res = hidden + residual`` (``hidden`` alone when
+    ``residual`` is None), then ``normed = RMSNorm(res, w)``. Returns
+    ``(res, normed)``.
+
+    "qwen3_dflash.cpp" page, ``ForwardBlockLogits`` / ``ForwardWithCtxKVDev``:
+    input_layernorm is the standard add + RMSNorm (the norm of hidden plus the
+    residual stream, which is updated to that sum).
+    """
+    h = _f64(hidden)
+    res = h if residual is None else h + _f64(residual)
+    return res, rms_norm(res, w, eps)
+
+
+def block_qkv(normed, w_qkv, num_q_heads, num_kv_heads, head_dim):
+    """Merged q/k/v projection of the block rows: ``qkv = normed @ w_qkv.T``.
+
+    ``w_qkv`` is ``[(Hq + 2 Hkv) * Dh, H]``; its rows are the q heads, then
+    the k heads, then the v heads, each head Dh consecutive rows. Returns raw
+    ``q [T, Hq, Dh]``, ``k [T, Hkv, Dh]``, ``v [T, Hkv, Dh]``.
+
+    "qwen3_dflash.cpp" page, ``ForwardBlockLogits``: one product against the
+    merged weight, then the split into q, k and v (the unmerged form takes the
+    row slices [0, qdim), [qdim, qdim + kdim), [qdim + kdim, qdim + 2 kdim)).
+    """
+    qkv = _f64(normed) @ _f64(w_qkv).T
+    t = qkv.shape[0]
+    qd = num_q_heads * head_dim
+    kd = num_kv_heads * head_dim
+    q = qkv[:, :qd].reshape(t, num_q_heads, head_dim)
+    k = qkv[:, qd:qd + kd].reshape(t, num_kv_heads, head_dim)
+    v = qkv[:, qd + kd:qd + 2 * kd].reshape(t, num_kv_heads, head_dim)
+    return q, k, v
+
+
+def output_projection(attn, w_o):
+    """o_proj: each row's attention output ``[Hq, Dh]`` read as one vector of
+    Hq * Dh (head-major), times ``w_o.T`` (``w_o`` is ``[H, Hq * Dh]``).
+
+    "qwen3_dflash.cpp" page, ``ForwardBlockLogits`` / ``ForwardWithCtxKVDev``:
+    the attention output reshaped to ``[T, Hq * Dh]`` and multiplied by the
+    o_proj weight (MatmulBT).
+    """
+    a = _f64(attn)
+    return a.reshape(a.shape[0], -1) @ _f64(w_o).T
+
+
+def draft_layer_attention(hidden, residual, in_norm_w, w_qkv, w_o, blk_positions,
+                          k_ctx_hat, v_ctx, cu_ctx, cu_blk, q_norm_w, k_norm_w,
+                          num_q_heads, num_kv_heads, head_dim, eps, theta, scale,
+                          causal=False, window=0):
+    """The draft layer's attention block: input_layernorm (residual add +
+    RMSNorm), merged q/k/v projection, q/k norm + RoPE, block attention over
+    [context; block], o_proj. Returns ``(o, res, q, k, v, attn)`` with q, k,
+    v the raw projections.
+
+    "qwen3_dflash.cpp" page, ``ForwardWithCtxKVDev``, in that order.
+    """
+    res, normed = residual_rms_norm(hidden, residual, in_norm_w, eps)
+    q, k, v = block_qkv(normed, w_qkv, num_q_heads, num_kv_heads, head_dim)
+    attn, _, _ = draft_block_attention(q, k, v, blk_positions, k_ctx_hat, v_ctx, cu_ctx, cu_blk,
+                                       q_norm_w, k_norm_w, eps, theta, scale, causal, window)
+    return output_projection(attn, w_o), res, q, k, v, attn

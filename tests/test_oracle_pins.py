@@ -554,3 +554,150 @@ def test_paged_rows_pin_catches_index_mistakes():
     for f in (wrong_offset, wrong_page):
         got = f(pool, bt, lens)
         assert not np.array_equal(got, rows)
+
+
+# ---------------------------------------------------------------- the layer around the attention
+
+def _layer_ns(**over):
+    base = dict(residual_rms_norm=O.residual_rms_norm, block_qkv=O.block_qkv,
+                output_projection=O.output_projection)
+    base.update(over)
+    return types.SimpleNamespace(**base)
+
+
+def lpin_residual_norm(X):
+    t, h = 6, 40
+    x = RNG.standard_normal((t, h))
+    r = RNG.standard_normal((t, h))
+    w = RNG.uniform(0.5, 1.5, h)
+    res, normed = X.residual_rms_norm(x, r, w, 1e-6)
+    assert np.array_equal(res, x + r)                   # the residual stream becomes the sum
+    ref = torch.nn.functional.rms_norm(torch.from_numpy(x + r), (h,), torch.from_numpy(w), eps=1e-6)
+    np.testing.assert_allclose(normed, ref.numpy(), rtol=1e-13, atol=1e-13)
+    res0, normed0 = X.residual_rms_norm(x, None, w, 1e-6)   # no residual: the norm of hidden
+    assert np.array_equal(res0, x)
+    ref0 = torch.nn.functional.rms_norm(torch.from_numpy(x), (h,), torch.from_numpy(w), eps=1e-6)
+    np.testing.assert_allclose(normed0, ref0.numpy(), rtol=1e-13, atol=1e-13)
+
+
+def lpin_block_qkv_split(X):
+    # the merged weight's row blocks, each applied by the library's linear
+    t, h, hq, hkv, d = 5, 24, 4, 2, 6
+    x = RNG.standard_normal((t, h))
+    wq = RNG.standard_normal((hq * d, h))
+    wk = RNG.standard_normal((hkv * d, h))
+    wv = RNG.standard_normal((hkv * d, h))
+    q, k, v = X.block_qkv(x, np.concatenate([wq, wk, wv]), hq, hkv, d)
+    lin = lambda w: torch.nn.functional.linear(torch.from_numpy(x), torch.from_numpy(w)).numpy()
+    np.testing.assert_allclose(q, lin(wq).reshape(t, hq, d), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(k, lin(wk).reshape(t, hkv, d), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(v, lin(wv).reshape(t, hkv, d), rtol=1e-12, atol=1e-12)
+    # head h of q is rows [h Dh, (h + 1) Dh) of the weight: a weight that is
+    # zero except one row of head 2 moves one input column to q[:, 2, e]
+    w = np.zeros(((hq + 2 * hkv) * d, h))
+    w[2 * d + 3, 7] = 1.0
+    q1, k1, v1 = X.block_qkv(x, w, hq, hkv, d)
+    assert np.array_equal(q1[:, 2, 3], x[:, 7]) and np.count_nonzero(q1) == np.count_nonzero(x[:, 7])
+    assert not k1.any() and not v1.any()
+
+
+def lpin_output_projection(X):
+    t, hq, d, hsz = 4, 3, 5, 7
+    a = RNG.standard_normal((t, hq, d))
+    w = RNG.standard_normal((hsz, hq * d))
+    ref = torch.nn.functional.linear(torch.from_numpy(a.reshape(t, hq * d)), torch.from_numpy(w))
+    np.testing.assert_allclose(X.output_projection(a, w), ref.numpy(), rtol=1e-12, atol=1e-12)
+    # head-major flattening: input column h * Dh + e is head h, element e
+    w1 = np.zeros((hsz, hq * d))
+    w1[0, 2 * d + 1] = 1.0
+    np.testing.assert_array_equal(X.output_projection(a, w1)[:, 0], a[:, 2, 1])
+
+
+def lpin_layer_reduces_to_attention(X):
+    # H = Hq Dh, q weight = identity, o_proj = identity, unit norm weight:
+    # the layer is the block attention of the normed rows with k = x Wk^T, v = x Wv^T
+    hq, hkv, d = 2, 1, 8
+    h = hq * d
+    cu_c = np.array([0, 5, 12])
+    cu_b = np.array([0, 3, 7])
+    t = int(cu_b[-1])
+    x = RNG.standard_normal((t, h))
+    wk = RNG.standard_normal((hkv * d, h)) * 0.3
+    wv = RNG.standard_normal((hkv * d, h)) * 0.3
+    w_qkv = np.concatenate([np.eye(h), wk, wv])
+    kc = RNG.standard_normal((int(cu_c[-1]), hkv, d))
+    vc = RNG.standard_normal((int(cu_c[-1]), hkv, d))
+    pos = np.concatenate([np.arange(c, c + b) for c, b in zip(np.diff(cu_c), np.diff(cu_b))])
+    ones = np.ones(d)
+    o, res, q, k, v, attn = O.draft_layer_attention(
+        x, None, np.ones(h), w_qkv, np.eye(h), pos, kc, vc, cu_c, cu_b, ones, ones, hq, hkv, d,
+        1e-6, 1e4, d ** -0.5)
+    _, normed = X.residual_rms_norm(x, None, np.ones(h), 1e-6)
+    ref, _, _ = O.draft_block_attention(normed.reshape(t, hq, d), (normed @ wk.T).reshape(t, hkv, d),
+                                        (normed @ wv.T).reshape(t, hkv, d), pos, kc, vc, cu_c, cu_b,
+                                        ones, ones, 1e-6, 1e4, d ** -0.5)
+    np.testing.assert_allclose(o, ref.reshape(t, h), rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(attn, ref, rtol=1e-12, atol=1e-12)
+
+
+LAYER_PINS = [lpin_residual_norm, lpin_block_qkv_split, lpin_output_projection,
+              lpin_layer_reduces_to_attention]
+
+
+@pytest.mark.parametrize("pin", LAYER_PINS, ids=[p.__name__ for p in LAYER_PINS])
+def test_layer_oracle_pin(pin):
+    pin(_layer_ns())
+
+
+def _lmut_no_residual(x, r, w, eps):
+    return O.residual_rms_norm(x, None, w, eps)
+
+
+def _lmut_norm_before_add(x, r, w, eps):
+    res, normed = O.residual_rms_norm(x, None, w, eps)
+    return (res if r is None else res + r), normed
+
+
+def _lmut_kv_swapped(x, w, hq, hkv, d):
+    q, k, v = O.block_qkv(x, w, hq, hkv, d)
+    return q, v, k
+
+
+def _lmut_heads_transposed(x, w, hq, hkv, d):
+    q, k, v = O.block_qkv(x, w, hq, hkv, d)
+    t = q.shape[0]
+    return q.reshape(t, d, hq).transpose(0, 2, 1), k, v
+
+
+def _lmut_oproj_dim_major(a, w):
+    a = np.asarray(a, np.float64)
+    return a.transpose(0, 2, 1).reshape(a.shape[0], -1) @ np.asarray(w, np.float64).T
+
+
+def _lmut_oproj_no_transpose(a, w):
+    a = np.asarray(a, np.float64)
+    w = np.asarray(w, np.float64)
+    return a.reshape(a.shape[0], -1) @ w.reshape(w.shape[1], w.shape[0])
+
+
+LAYER_MUTANTS = {
+    "residual_dropped": dict(residual_rms_norm=_lmut_no_residual),
+    "norm_before_residual_add": dict(residual_rms_norm=_lmut_norm_before_add),
+    "qkv_k_v_swapped": dict(block_qkv=_lmut_kv_swapped),
+    "qkv_heads_transposed": dict(block_qkv=_lmut_heads_transposed),
+    "oproj_dim_major_flatten": dict(output_projection=_lmut_oproj_dim_major),
+    "oproj_weight_not_transposed": dict(output_projection=_lmut_oproj_no_transpose),
+}
+
+
+@pytest.mark.parametrize("name", sorted(LAYER_MUTANTS))
+def test_layer_pins_catch_planted_mistakes(name):
+    ns = _layer_ns(**LAYER_MUTANTS[name])
+    failed = False
+    for pin in LAYER_PINS:
+        try:
+            pin(ns)
+        except (AssertionError, ValueError):
+            failed = True
+            break
+    assert failed, f"no layer pin detects mutant {name}"
