@@ -38,6 +38,10 @@ EXPORTED = (
     "dflash_block_attention_paged",
     "dflash_block_attention_paged_workspace_size",
     "dflash_kv_scatter",
+    "dflash_block_qkv_workspace_size",
+    "dflash_block_qkv",
+    "dflash_o_proj_workspace_size",
+    "dflash_o_proj",
 )
 
 
@@ -135,6 +139,14 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dflash_block_attention_paged_workspace_size.argtypes = [ctypes.POINTER(BlockAttnParams)]
     lib.dflash_kv_scatter.restype = ctypes.c_int
     lib.dflash_kv_scatter.argtypes = [ctypes.c_int, P, P, P, I64, I32, I32, P, P, I64, P]
+    lib.dflash_block_qkv_workspace_size.restype = SZ
+    lib.dflash_block_qkv_workspace_size.argtypes = [I64, I32, I32, I32, I32]
+    lib.dflash_block_qkv.restype = ctypes.c_int
+    lib.dflash_block_qkv.argtypes = [P, P, P, P, I64, I32, I32, I32, I32, F, P, P, P, P, SZ, P]
+    lib.dflash_o_proj_workspace_size.restype = SZ
+    lib.dflash_o_proj_workspace_size.argtypes = [I64, I32, I32]
+    lib.dflash_o_proj.restype = ctypes.c_int
+    lib.dflash_o_proj.argtypes = [P, P, I64, I32, I32, P, P, SZ, P]
     _lib = lib
     return lib
 
@@ -310,3 +322,38 @@ def dflash_kv_scatter(k_src: torch.Tensor, v_src: torch.Tensor, slot_mapping: to
     _check(lib.dflash_kv_scatter(_dtype_code(k_src), _ptr(k_src), _ptr(v_src), _ptr(slot_mapping),
                                  t, hkv, dh, _ptr(k_pool), _ptr(v_pool), num_slots,
                                  _stream(stream)))
+
+
+def dflash_block_qkv_workspace_size(T: int, hidden_size: int, num_q_heads: int,
+                                    num_kv_heads: int, head_dim: int) -> int:
+    return load().dflash_block_qkv_workspace_size(T, hidden_size, num_q_heads, num_kv_heads,
+                                                  head_dim)
+
+
+def dflash_block_qkv(hidden: torch.Tensor, residual: Optional[torch.Tensor], norm_w: torch.Tensor,
+                     w_qkv: torch.Tensor, num_q_heads: int, num_kv_heads: int, head_dim: int,
+                     eps: float, q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                     workspace: Optional[torch.Tensor], stream=None) -> None:
+    """Input norm (residual add + RMSNorm) and the merged q/k/v projection of
+    ``hidden [T, H]``; q, k, v are written raw."""
+    lib = load()
+    t, h = hidden.shape
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dflash_block_qkv(_ptr(hidden), _ptr(residual), _ptr(norm_w), _ptr(w_qkv), t, h,
+                                num_q_heads, num_kv_heads, head_dim, float(eps), _ptr(q), _ptr(k),
+                                _ptr(v), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dflash_o_proj_workspace_size(T: int, hidden_size: int, in_dim: int) -> int:
+    return load().dflash_o_proj_workspace_size(T, hidden_size, in_dim)
+
+
+def dflash_o_proj(attn: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor,
+                  workspace: Optional[torch.Tensor], stream=None) -> None:
+    """``out [T, H] = attn [T, in_dim] @ w_o [H, in_dim]^T`` (attn may be [T, Hq, Dh])."""
+    lib = load()
+    t = attn.shape[0]
+    in_dim = attn.numel() // max(t, 1) if t > 0 else w_o.shape[1]
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dflash_o_proj(_ptr(attn), _ptr(w_o), t, w_o.shape[0], in_dim, _ptr(out),
+                             _ptr(workspace), ws_bytes, _stream(stream)))

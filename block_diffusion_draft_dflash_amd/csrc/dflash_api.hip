@@ -62,7 +62,7 @@ extern "C" {
 
 const char* dflash_last_error(void) { return g_last_error.c_str(); }
 
-int dflash_abi_version(void) { return 102; }
+int dflash_abi_version(void) { return 103; }
 
 dflash_status dflash_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
                                 void* stream) {
@@ -338,6 +338,77 @@ dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, 
                                               rope_table, max_pos, k_out, v_out, workspace,
                                               (hipStream_t)stream),
                     "context_kv launch");
+}
+
+size_t dflash_block_qkv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim) {
+  if (T < 0 || hidden_size < 64 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1) return 0;
+  return dflash::block_qkv_workspace_bytes(T, hidden_size, num_q_heads, num_kv_heads, head_dim,
+                                           kPlanComputeUnits);
+}
+
+dflash_status dflash_block_qkv(const void* hidden, void* residual, const float* norm_w,
+                               const void* w_qkv, int64_t T, int32_t hidden_size,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float eps, void* q, void* k, void* v, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  if (T < 0 || T > INT32_MAX) return fail(DFLASH_ERR_INVALID_ARG, "block_qkv: T must be in [0, 2^31)");
+  if (num_q_heads < 1 || num_kv_heads < 1 || num_q_heads % num_kv_heads != 0)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_qkv: need Hq >= 1, Hkv >= 1 and Hq %% Hkv == 0");
+  if (head_dim != 64 && head_dim != 128)
+    return fail(DFLASH_ERR_UNSUPPORTED, "block_qkv: head_dim %d is not supported (64 or 128)", head_dim);
+  if (hidden_size < 64 || hidden_size % 64 != 0 || hidden_size > 8192)
+    return fail(DFLASH_ERR_UNSUPPORTED, "block_qkv: hidden_size must be a multiple of 64 in [64, 8192]");
+  if ((int64_t)(num_q_heads + 2 * num_kv_heads) * head_dim > INT32_MAX / 2)
+    return fail(DFLASH_ERR_INVALID_ARG, "block_qkv: too many heads");
+  if (!(eps >= 0.f) || !std::isfinite(eps))
+    return fail(DFLASH_ERR_INVALID_ARG, "block_qkv: eps must be finite and >= 0");
+  if (T == 0) return ok();
+  const void* ptrs[] = {hidden, norm_w, w_qkv, q, k, v};
+  for (const void* t : ptrs)
+    if (!t) return fail(DFLASH_ERR_INVALID_ARG, "block_qkv: NULL pointer argument");
+  const void* al[] = {hidden, norm_w, w_qkv, q, k, v, residual};
+  for (const void* t : al)
+    if (t && !aligned(t, 16)) return fail(DFLASH_ERR_INVALID_ARG, "block_qkv: tensors must be 16-byte aligned");
+  const size_t need = dflash::block_qkv_workspace_bytes(T, hidden_size, num_q_heads, num_kv_heads,
+                                                        head_dim, kPlanComputeUnits);
+  if (!workspace) return fail(DFLASH_ERR_WORKSPACE, "block_qkv: workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(workspace, 256)) return fail(DFLASH_ERR_WORKSPACE, "block_qkv: workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(DFLASH_ERR_WORKSPACE, "block_qkv: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_status(dflash::launch_block_qkv(hidden, residual, norm_w, w_qkv, T, hidden_size,
+                                             num_q_heads, num_kv_heads, head_dim, eps, q, k, v,
+                                             workspace, kPlanComputeUnits, (hipStream_t)stream),
+                    "block_qkv launch");
+}
+
+size_t dflash_o_proj_workspace_size(int64_t T, int32_t hidden_size, int32_t in_dim) {
+  if (T < 0 || hidden_size < 64 || in_dim < 64) return 0;
+  return dflash::o_proj_workspace_bytes(T, hidden_size, in_dim, kPlanComputeUnits);
+}
+
+dflash_status dflash_o_proj(const void* attn, const void* w_o, int64_t T, int32_t hidden_size,
+                            int32_t in_dim, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream) {
+  if (T < 0 || T > INT32_MAX) return fail(DFLASH_ERR_INVALID_ARG, "o_proj: T must be in [0, 2^31)");
+  if (hidden_size < 64 || hidden_size % 64 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "o_proj: hidden_size must be a positive multiple of 64");
+  if (in_dim < 64 || in_dim % 64 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "o_proj: in_dim must be a positive multiple of 64");
+  if (T == 0) return ok();
+  if (!attn || !w_o || !out) return fail(DFLASH_ERR_INVALID_ARG, "o_proj: NULL pointer argument");
+  if (!aligned(attn, 16) || !aligned(w_o, 16) || !aligned(out, 16))
+    return fail(DFLASH_ERR_INVALID_ARG, "o_proj: tensors must be 16-byte aligned");
+  const size_t need = dflash::o_proj_workspace_bytes(T, hidden_size, in_dim, kPlanComputeUnits);
+  if (need > 0) {
+    if (!workspace) return fail(DFLASH_ERR_WORKSPACE, "o_proj: workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(workspace, 256)) return fail(DFLASH_ERR_WORKSPACE, "o_proj: workspace must be 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(DFLASH_ERR_WORKSPACE, "o_proj: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  return hip_status(dflash::launch_o_proj(attn, w_o, T, hidden_size, in_dim, out, workspace,
+                                          kPlanComputeUnits, (hipStream_t)stream),
+                    "o_proj launch");
 }
 
 }  // extern "C"

@@ -45,4 +45,14 @@ hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* w
                              const float* table, int32_t max_pos, void* k_out, void* v_out,
                              void* ws, hipStream_t s);
 
+size_t block_qkv_workspace_bytes(int64_t T, int32_t hidden, int32_t hq, int32_t hkv, int32_t dh,
+                                 int num_cus);
+hipError_t launch_block_qkv(const void* hidden, void* residual, const float* norm_w,
+                            const void* w_qkv, int64_t T, int32_t hidden_size, int32_t hq,
+                            int32_t hkv, int32_t dh, float eps, void* q, void* k, void* v,
+                            void* ws, int num_cus, hipStream_t s);
+size_t o_proj_workspace_bytes(int64_t T, int32_t hidden, int32_t in_dim, int num_cus);
+hipError_t launch_o_proj(const void* attn, const void* w_o, int64_t T, int32_t hidden,
+                         int32_t in_dim, void* out, void* ws, int num_cus, hipStream_t s);
+
 }  // namespace dflash

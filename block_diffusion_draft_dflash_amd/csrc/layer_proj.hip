@@ -1,0 +1,398 @@
+// The draft layer's projections around the block attention.
+//
+// "qwen3_dflash.cpp" page, ForwardBlockLogits and ForwardWithCtxKVDev:
+// input_layernorm is the standard residual add + RMSNorm (the residual stream
+// becomes hidden + residual, the normed rows are a bf16 tensor), the normed
+// block rows go through one product with the merged qkv weight whose row
+// blocks are the q, k and v heads, and after the attention the output rows
+// [T, Hq * Dh] go through the o_proj weight. Both products are x * W^T with
+// W row-major [out, in].
+//
+// Kernels:
+//   residual_norm_kernel  one workgroup per row: res = hidden (+ residual,
+//                         stored back as bf16), normed = bf16(res * rstd * w).
+//   proj_gemm_kernel      C[T, N] = A[T, K] * W[N, K]^T on bf16 MFMA with f32
+//                         accumulation. A workgroup owns a 128 x 64 output tile
+//                         and a slice of K; K advances 64 at a time through a
+//                         ring of LDS stages filled by direct HBM -> LDS copies
+//                         (XOR-swizzled 128-byte rows, explicit waits). With
+//                         few tiles (T ~ 128: the weights are the bytes) K is
+//                         split so that every CU streams a share of the weight;
+//                         the slices then write f32 partial tiles.
+//   split_sum_kernel      sums the K-slice partials and rounds to bf16.
+// Output columns go to up to three row-major destinations (q | k | v).
+#include <algorithm>
+#include <mutex>
+
+#include "dflash_device.h"
+#include "dflash_internal.h"
+
+namespace dflash {
+namespace {
+
+constexpr int GBM = 128;  // output rows per workgroup tile
+constexpr int GBN = 64;   // output columns per workgroup tile
+constexpr int GBK = 64;   // K per ring stage (two MFMA k-steps of 32)
+constexpr int GNT = 256;  // threads (4 waves; wave w owns rows 32 w .. 32 w + 31)
+constexpr int GNS = 3;    // ring stages: GNS - 1 in flight
+constexpr int A_TILE = GBM * GBK;
+constexpr int W_TILE = GBN * GBK;
+constexpr int G_STAGE = A_TILE + W_TILE;  // bf16 elements per stage (24 KB)
+constexpr int LPS = (A_TILE + W_TILE) / 512 / (GNT / 64);  // wave-wide 1 KB copies per wave per stage
+constexpr int NORM_MAX_CHUNKS = 4;  // 8-element chunks per thread in the row norm (H <= 8192)
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+// s_waitcnt takes an immediate: at most k * STEP vector-memory operations
+// outstanding, for a run-time k clamped to [0, MAXK].
+template <int STEP, int MAXK>
+__device__ __forceinline__ void wait_vmcnt_steps(int32_t k) {
+  if constexpr (MAXK > 0) {
+    if (k >= MAXK) {
+      wait_vmcnt<MAXK * STEP>();
+      return;
+    }
+    wait_vmcnt_steps<STEP, MAXK - 1>(k);
+  } else {
+    wait_vmcnt<0>();
+  }
+}
+// Workgroup barrier without the fence of __syncthreads (which would drain the
+// copies still in flight).
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+// One wave-wide 16-byte-per-lane copy HBM -> LDS: lane l's 16 bytes land at
+// dst + 16 l (dst is the wave's 1 KB destination). Issued from inline
+// assembly so that the compiler does not drain it before every LDS read;
+// every wait on it is explicit.
+__device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
+// Physical 16-byte chunk of logical chunk c in a 128-byte LDS row.
+__device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
+
+struct OutSegs {
+  bf16* ptr[3];
+  int64_t stride[3];  // elements between consecutive rows
+  int32_t begin[4];   // segment s holds columns [begin[s], begin[s + 1])
+};
+
+__device__ __forceinline__ int seg_of(const OutSegs& o, int32_t n) {
+  return n >= o.begin[2] ? 2 : (n >= o.begin[1] ? 1 : 0);
+}
+
+// ---------------------------------------------------------------------------
+// input_layernorm: residual add + RMSNorm, one workgroup per row.
+template <bool RES>
+__global__ __launch_bounds__(256) void residual_norm_kernel(const bf16* __restrict__ hidden,
+                                                            bf16* __restrict__ residual,
+                                                            const float* __restrict__ w,
+                                                            bf16* __restrict__ normed, int32_t H,
+                                                            float eps) {
+  __shared__ float red[4];
+  const int64_t t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int nch = H / 8;
+  float x[NORM_MAX_CHUNKS][8];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NORM_MAX_CHUNKS; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nch) {
+      const bf16x8 h = *reinterpret_cast<const bf16x8*>(hidden + t * H + 8 * c);
+      if constexpr (RES) {
+        // the residual stream becomes hidden + residual (stored as bf16);
+        // the norm reads the stored value
+        bf16x8* rp = reinterpret_cast<bf16x8*>(residual + t * H + 8 * c);
+        const bf16x8 r = *rp;
+        bf16x8 s;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] = f2bf(bf2f(h[e]) + bf2f(r[e]));
+        *rp = s;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = bf2f(s[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[i][e] = bf2f(h[e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) ss += x[i][e] * x[i][e];
+    }
+  }
+  ss = group_sum<64>(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float rstd = 1.0f / sqrtf(tot / (float)H + eps);
+#pragma unroll
+  for (int i = 0; i < NORM_MAX_CHUNKS; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nch) {
+      const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * c);
+      const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * c + 4);
+      const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+      bf16x8 o;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] = f2bf(x[i][e] * rstd * wv[e]);
+      *reinterpret_cast<bf16x8*>(normed + t * H + 8 * c) = o;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// C = A * W^T over one K slice of one 128 x 64 tile.
+struct GemmArgs {
+  const bf16* a;  // [T, K]
+  const bf16* w;  // [N, K]
+  int64_t T;
+  int32_t N, K, kslice, nsplit;
+  float* part;  // [nsplit][T][N] f32 when nsplit > 1
+  OutSegs out;
+};
+
+__global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];
+  const int32_t ntn = g.N / GBN;
+  int64_t id = blockIdx.x;
+  const int32_t nt = (int32_t)(id % ntn);
+  id /= ntn;
+  const int32_t ks = (int32_t)(id % g.nsplit);
+  const int64_t mt = id / g.nsplit;
+  const int64_t m0 = mt * GBM;
+  const int32_t n0 = nt * GBN;
+  const int32_t kbeg = ks * g.kslice;
+  const int32_t nk = g.kslice / GBK;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int m = lane & 15;
+  const int j = lane >> 4;
+
+  // Copy lanes: one wave-wide copy fills 8 rows of 128 bytes; lane l fetches
+  // the logical chunk that the swizzle puts at (row l / 8, chunk l % 8).
+  // Rows past T re-read row T - 1 (their results are never stored).
+  const int r8 = lane >> 3, pc = lane & 7;
+  int64_t a_src[4];
+  int64_t w_src[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = (w * 4 + i) * 8 + r8;
+    const int64_t grow = min(m0 + row, g.T - 1);
+    a_src[i] = grow * g.K + swz(row, pc) * 8;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int row = (w * 2 + i) * 8 + r8;
+    w_src[i] = (int64_t)(n0 + row) * g.K + swz(row, pc) * 8;
+  }
+  auto issue = [&](int32_t kt) {
+    const int32_t k0 = kbeg + kt * GBK;
+    bf16* st = smem + (kt % GNS) * G_STAGE;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds_copy16(g.a + a_src[i] + k0, st + (w * 4 + i) * 8 * GBK);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) lds_copy16(g.w + w_src[i] + k0, st + A_TILE + (w * 2 + i) * 8 * GBK);
+  };
+
+  f32x4 acc[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int kt = 0; kt < GNS - 1; ++kt)
+    if (kt < nk) issue(kt);
+  for (int32_t kt = 0; kt < nk; ++kt) {
+    // own copies of stage kt landed (later stages may stay in flight); the
+    // barrier makes every wave's part visible and frees stage kt - 1
+    wait_vmcnt_steps<LPS, GNS - 2>(nk - 1 - kt);
+    block_barrier();
+    if (kt + GNS - 1 < nk) issue(kt + GNS - 1);
+    const bf16* st = smem + (kt % GNS) * G_STAGE;
+#pragma unroll
+    for (int ss = 0; ss < 2; ++ss) {
+      const int c = 4 * ss + j;  // logical 16-byte chunk (k = 8 c .. 8 c + 7)
+      bf16x8 af[2], bf[4];
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt) {
+        const int row = 32 * w + 16 * rt + m;
+        af[rt] = *reinterpret_cast<const bf16x8*>(st + row * GBK + swz(row, c) * 8);
+      }
+#pragma unroll
+      for (int ct = 0; ct < 4; ++ct) {
+        const int row = 16 * ct + m;
+        bf[ct] = *reinterpret_cast<const bf16x8*>(st + A_TILE + row * GBK + swz(row, c) * 8);
+      }
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+          acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt], bf[ct], acc[rt][ct], 0, 0, 0);
+    }
+  }
+
+  // lane (m, j): acc[rt][ct][i] = C[m0 + 32 w + 16 rt + 4 j + i][n0 + 16 ct + m]
+  if (g.nsplit == 1) {
+    const int sg = seg_of(g.out, n0);
+    bf16* base = g.out.ptr[sg];
+    const int64_t stride = g.out.stride[sg];
+    const int32_t col = n0 - g.out.begin[sg];
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = m0 + 32 * w + 16 * rt + 4 * j + i;
+        if (t < g.T) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) base[t * stride + col + 16 * ct + m] = f2bf(acc[rt][ct][i]);
+        }
+      }
+  } else {
+    float* p = g.part + (int64_t)ks * g.T * g.N;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t = m0 + 32 * w + 16 * rt + 4 * j + i;
+        if (t < g.T) {
+#pragma unroll
+          for (int ct = 0; ct < 4; ++ct) p[t * g.N + n0 + 16 * ct + m] = acc[rt][ct][i];
+        }
+      }
+  }
+}
+
+// Sum of the K-slice partials, 8 columns a thread, in slice order.
+__global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part,
+                                                        int32_t nsplit, int64_t T, int32_t N,
+                                                        OutSegs out) {
+  const int64_t n8 = N / 8;
+  const int64_t total = T * n8;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t t = i / n8;
+    const int32_t n = (int32_t)(i - t * n8) * 8;
+    float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int32_t k = 0; k < nsplit; ++k) {
+      const float4* p = reinterpret_cast<const float4*>(part + ((int64_t)k * T + t) * N + n);
+      const float4 a = p[0], b = p[1];
+      s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
+      s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+    }
+    const int sg = seg_of(out, n);
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = f2bf(s[e]);
+    *reinterpret_cast<bf16x8*>(out.ptr[sg] + t * out.stride[sg] + (n - out.begin[sg])) = o;
+  }
+}
+
+struct ProjPlan {
+  int64_t mtiles;
+  int32_t ntiles, nsplit, kslice;
+  size_t part_bytes;
+};
+
+// K is split (in powers of two, slices of at least 256) until the tiles
+// cover the CUs.
+ProjPlan plan_proj(int64_t T, int32_t N, int32_t K, int num_cus) {
+  ProjPlan pl{};
+  pl.mtiles = (T + GBM - 1) / GBM;
+  pl.ntiles = N / GBN;
+  pl.nsplit = 1;
+  const int64_t tiles = pl.mtiles * pl.ntiles;
+  while (tiles * pl.nsplit < num_cus && K % (pl.nsplit * 2 * GBK) == 0 && K / (pl.nsplit * 2) >= 256)
+    pl.nsplit *= 2;
+  pl.kslice = K / pl.nsplit;
+  pl.part_bytes = pl.nsplit > 1 ? (size_t)pl.nsplit * (size_t)T * (size_t)N * sizeof(float) : 0;
+  return pl;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+hipError_t launch_proj(const bf16* a, const bf16* w, int64_t T, int32_t N, int32_t K,
+                       const ProjPlan& pl, float* part, const OutSegs& out, hipStream_t s) {
+  // 72 KB of LDS per workgroup (three stages). The limit is a per-function
+  // setting: raised once per device, not per launch (stream capture then
+  // sees only the launches).
+  static std::once_flag once[64];
+  int dev = 0;
+  (void)hipGetDevice(&dev);
+  std::call_once(once[dev & 63], [] {
+    (void)hipFuncSetAttribute((const void*)proj_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
+                              GNS * G_STAGE * (int)sizeof(bf16));
+  });
+  GemmArgs g{};
+  g.a = a; g.w = w; g.T = T; g.N = N; g.K = K;
+  g.kslice = pl.kslice; g.nsplit = pl.nsplit; g.part = part; g.out = out;
+  const int64_t blocks = pl.mtiles * pl.ntiles * pl.nsplit;
+  hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)blocks), dim3(GNT),
+                     (size_t)GNS * G_STAGE * sizeof(bf16), s, g);
+  if (pl.nsplit > 1) {
+    const int64_t items = T * (N / 8);
+    const int64_t sblocks = std::min<int64_t>((items + 255) / 256, 4096);
+    hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)sblocks), dim3(256), 0, s,
+                       (const float*)part, pl.nsplit, T, N, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t block_qkv_workspace_bytes(int64_t T, int32_t hidden, int32_t hq, int32_t hkv, int32_t dh,
+                                 int num_cus) {
+  const int32_t n = (hq + 2 * hkv) * dh;
+  const ProjPlan pl = plan_proj(T, n, hidden, num_cus);
+  return align256((size_t)T * hidden * sizeof(bf16)) + align256(pl.part_bytes);
+}
+
+hipError_t launch_block_qkv(const void* hidden, void* residual, const float* norm_w,
+                            const void* w_qkv, int64_t T, int32_t hidden_size, int32_t hq,
+                            int32_t hkv, int32_t dh, float eps, void* q, void* k, void* v,
+                            void* ws, int num_cus, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  bf16* normed = (bf16*)ws;
+  const int32_t n = (hq + 2 * hkv) * dh;
+  const ProjPlan pl = plan_proj(T, n, hidden_size, num_cus);
+  float* part = (float*)((char*)ws + align256((size_t)T * hidden_size * sizeof(bf16)));
+  if (residual)
+    hipLaunchKernelGGL(residual_norm_kernel<true>, dim3((unsigned)T), dim3(256), 0, s,
+                       (const bf16*)hidden, (bf16*)residual, norm_w, normed, hidden_size, eps);
+  else
+    hipLaunchKernelGGL(residual_norm_kernel<false>, dim3((unsigned)T), dim3(256), 0, s,
+                       (const bf16*)hidden, (bf16*)nullptr, norm_w, normed, hidden_size, eps);
+  OutSegs out{};
+  out.ptr[0] = (bf16*)q; out.ptr[1] = (bf16*)k; out.ptr[2] = (bf16*)v;
+  out.stride[0] = (int64_t)hq * dh; out.stride[1] = (int64_t)hkv * dh; out.stride[2] = (int64_t)hkv * dh;
+  out.begin[0] = 0; out.begin[1] = hq * dh; out.begin[2] = (hq + hkv) * dh; out.begin[3] = n;
+  return launch_proj(normed, (const bf16*)w_qkv, T, n, hidden_size, pl, part, out, s);
+}
+
+size_t o_proj_workspace_bytes(int64_t T, int32_t hidden, int32_t in_dim, int num_cus) {
+  return align256(plan_proj(T, hidden, in_dim, num_cus).part_bytes);
+}
+
+hipError_t launch_o_proj(const void* attn, const void* w_o, int64_t T, int32_t hidden,
+                         int32_t in_dim, void* out, void* ws, int num_cus, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const ProjPlan pl = plan_proj(T, hidden, in_dim, num_cus);
+  OutSegs o{};
+  o.ptr[0] = o.ptr[1] = o.ptr[2] = (bf16*)out;
+  o.stride[0] = o.stride[1] = o.stride[2] = hidden;
+  o.begin[0] = 0; o.begin[1] = o.begin[2] = o.begin[3] = hidden;
+  return launch_proj((const bf16*)attn, (const bf16*)w_o, T, hidden, in_dim, pl, (float*)ws, o, s);
+}
+
+}  // namespace dflash

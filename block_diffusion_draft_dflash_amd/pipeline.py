@@ -7,7 +7,10 @@ through the C ABI:
 * context rows: ``dflash_context_kv`` from hidden states when the workload has
   them, else the K-only ``dflash_qk_norm_rope`` on the raw context keys;
 * the step: ``dflash_qk_norm_rope`` on the block's q and k (in place), then
-  ``dflash_block_attention`` over [context; block]; or the one fused call.
+  ``dflash_block_attention`` over [context; block]; or the one fused call;
+* the draft layer around it (:class:`LayerPath`): ``dflash_block_qkv`` (input
+  norm and merged q/k/v projection of the block rows), the fused attention,
+  ``dflash_o_proj``.
 
 By default the host copies of the cumulative lengths go with the attention
 parameters (the work split is then planned on the host); ``host_lengths=False``
@@ -23,7 +26,7 @@ import numpy as np
 import torch
 
 from . import binding as B
-from .workloads import Workload, f32_to_bf16_bits
+from .workloads import LayerInputs, Workload, f32_to_bf16_bits
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -193,3 +196,57 @@ class DevicePath:
     def step_fused(self) -> None:
         """One pass of the hot path as a single fused call (bf16)."""
         self.attention_fused()
+
+
+class LayerPath:
+    """The draft layer's attention block on the GPU: input norm + merged q/k/v
+    projection of the block rows, the attention with the fused q/k norm +
+    RoPE over [context; block], o_proj. The context rows come from
+    ``DevicePath`` (packed store)."""
+
+    def __init__(self, wl: Workload, li: LayerInputs, device: str = "cuda",
+                 use_residual: bool = True):
+        if wl.dtype != "bf16":
+            raise ValueError("the layer path is bf16")
+        self.wl, self.li = wl, li
+        self.dp = DevicePath(wl, device)
+        self.dp.prepare_context()
+        t, h = wl.total_blk, li.hidden_size
+        self.hidden = bits_to_device(li.hidden, device)
+        self.residual_init = bits_to_device(li.residual, device) if use_residual else None
+        self.residual = None if self.residual_init is None else self.residual_init.clone()
+        self.in_norm_w = torch.from_numpy(np.ascontiguousarray(li.in_norm_w, np.float32)).to(device)
+        self.w_qkv = bits_to_device(li.w_qkv, device)
+        self.w_o = bits_to_device(li.w_o, device)
+        bf = torch.bfloat16
+        self.q = torch.empty((t, wl.hq, wl.dh), dtype=bf, device=device)
+        self.k = torch.empty((t, wl.hkv, wl.dh), dtype=bf, device=device)
+        self.v = torch.empty((t, wl.hkv, wl.dh), dtype=bf, device=device)
+        self.o = torch.empty((t, h), dtype=bf, device=device)
+        self.ws_qkv = B.alloc_workspace(
+            B.dflash_block_qkv_workspace_size(t, h, wl.hq, wl.hkv, wl.dh), device)
+        self.ws_o = B.alloc_workspace(B.dflash_o_proj_workspace_size(t, h, wl.hq * wl.dh), device)
+
+    def reset_residual(self) -> None:
+        if self.residual is not None:
+            self.residual.copy_(self.residual_init)
+
+    def qkv(self) -> None:
+        B.dflash_block_qkv(self.hidden, self.residual, self.in_norm_w, self.w_qkv, self.wl.hq,
+                           self.wl.hkv, self.wl.dh, self.wl.eps, self.q, self.k, self.v,
+                           self.ws_qkv)
+
+    def attention(self) -> None:
+        dp = self.dp
+        B.dflash_block_attention(dp.params, dp.cu_ctx, dp.cu_blk, self.q, self.k, self.v,
+                                 dp.k_ctx if self.wl.total_ctx > 0 else None,
+                                 dp.v_ctx if self.wl.total_ctx > 0 else None, dp.out, dp.ws,
+                                 prologue=dp.prologue)
+
+    def o_proj(self) -> None:
+        B.dflash_o_proj(self.dp.out, self.w_o, self.o, self.ws_o)
+
+    def step(self) -> None:
+        self.qkv()
+        self.attention()
+        self.o_proj()

@@ -28,6 +28,8 @@ __all__ = [
     "Workload",
     "CONFIGS",
     "make_workload",
+    "LayerInputs",
+    "make_layer_inputs",
     "f32_to_bf16_bits",
     "bf16_bits_to_f32",
 ]
@@ -219,3 +221,34 @@ def make_workload(name: str, seed: Optional[int] = None, **over) -> Workload:
         wl.w_v = f32_to_bf16_bits(rng.standard_normal((kdim, hidden_size), dtype=np.float32)
                                   * np.float32(0.02))
     return wl
+
+
+@dataclasses.dataclass
+class LayerInputs:
+    """Inputs of the draft layer around the attention for a workload's block
+    rows (bf16 bits as uint16; float arrays exactly bf16-representable)."""
+
+    hidden_size: int
+    hidden: np.ndarray        # [T, H] bf16 bits: the block rows' hidden states
+    residual: np.ndarray      # [T, H] bf16 bits: the residual stream before the layer
+    in_norm_w: np.ndarray     # [H] input_layernorm weight
+    w_qkv: np.ndarray         # [(Hq + 2 Hkv) Dh, H] bf16 bits: rows q heads | k heads | v heads
+    w_o: np.ndarray           # [H, Hq Dh] bf16 bits
+
+
+def make_layer_inputs(wl: Workload, hidden_size: int, seed: Optional[int] = None) -> LayerInputs:
+    """Draw the layer inputs for ``wl``'s block rows from a generator of their
+    own (the workload's own draws are unchanged): hidden and residual ~N(0, 1),
+    the norm weight ~U(0.5, 1.5), the projection weights ~N(0, 0.02), in that
+    order, all rounded to bf16."""
+    rng = np.random.default_rng(seed if seed is not None else 5000 + hidden_size + wl.total_blk)
+    t = wl.total_blk
+    n_qkv = (wl.hq + 2 * wl.hkv) * wl.dh
+    hid = f32_to_bf16_bits(rng.standard_normal((t, hidden_size), dtype=np.float32))
+    res = f32_to_bf16_bits(rng.standard_normal((t, hidden_size), dtype=np.float32))
+    w_in = _draw(rng, (hidden_size,), "bf16", "uniform", 0.5, 1.5)
+    w_qkv = f32_to_bf16_bits(rng.standard_normal((n_qkv, hidden_size), dtype=np.float32)
+                             * np.float32(0.02))
+    w_o = f32_to_bf16_bits(rng.standard_normal((hidden_size, wl.hq * wl.dh), dtype=np.float32)
+                           * np.float32(0.02))
+    return LayerInputs(hidden_size, hid, res, w_in, w_qkv, w_o)

@@ -293,6 +293,59 @@ dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, 
                                 int32_t max_pos, void* k_out, void* v_out, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
+/*
+ * dflash_block_qkv -- the draft layer's input norm and merged q/k/v
+ * projection of the block rows (bf16).
+ *
+ * For each block row t: res = hidden[t] + residual[t] (rounded to bf16 and
+ * written back to residual; with residual == NULL, res = hidden[t] and nothing
+ * is written), n = bf16(RMSNorm(res, norm_w)), qkv = n W_qkv^T, split into
+ * q | k | v by column: columns [0, Hq Dh) are q, the next Hkv Dh are k, the
+ * last Hkv Dh are v. q and k are the raw projections: the q/k RMSNorm and
+ * RoPE are the attention's fused prologue (dflash_qk_prologue) or
+ * dflash_qk_norm_rope. "qwen3_dflash.cpp" page, ForwardBlockLogits /
+ * ForwardWithCtxKVDev (input_layernorm as the standard add + RMSNorm, the
+ * merged qkv weight as one product, then the q/k/v split).
+ *
+ *   hidden     bf16 [T, H];  residual bf16 [T, H] (in/out) or NULL
+ *   norm_w     f32 [H] (the input_layernorm weight)
+ *   w_qkv      bf16 [(Hq + 2 Hkv) Dh, H], row-major (rows: q heads, k heads, v heads)
+ *   q          bf16 [T, Hq, Dh];  k, v bf16 [T, Hkv, Dh] (written)
+ *   workspace  device, 256-byte aligned, >= dflash_block_qkv_workspace_size
+ *              bytes (no zero-fill needed): the normed rows and, for small T,
+ *              f32 partial products of a split over H
+ * Requirements: Dh in {64, 128}, Hq % Hkv == 0, H % 64 == 0, H <= 8192; all
+ * tensors 16-byte aligned. T may be 0 (nothing is enqueued). Rows are
+ * independent. The caller owns every buffer; the call is asynchronous on
+ * `stream` and allocates nothing.
+ */
+size_t dflash_block_qkv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_q_heads,
+                                       int32_t num_kv_heads, int32_t head_dim);
+dflash_status dflash_block_qkv(const void* hidden, void* residual, const float* norm_w,
+                               const void* w_qkv, int64_t T, int32_t hidden_size,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                               float eps, void* q, void* k, void* v, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
+/*
+ * dflash_o_proj -- the draft layer's output projection (bf16).
+ *
+ * out[t] = attn[t] W_o^T, where attn[t] is the attention output row [Hq, Dh]
+ * read as one vector of in_dim = Hq Dh (head-major) and W_o is [H, in_dim].
+ * "qwen3_dflash.cpp" page, ForwardBlockLogits / ForwardWithCtxKVDev (o_proj
+ * applied to the attention output reshaped to [T, Hq Dh]).
+ *
+ *   attn       bf16 [T, in_dim];  w_o bf16 [H, in_dim];  out bf16 [T, H] (written)
+ *   workspace  device, 256-byte aligned, >= dflash_o_proj_workspace_size bytes
+ *              (may be 0 bytes and NULL when that is 0)
+ * Requirements: H % 64 == 0, in_dim % 64 == 0; tensors 16-byte aligned. T may
+ * be 0.
+ */
+size_t dflash_o_proj_workspace_size(int64_t T, int32_t hidden_size, int32_t in_dim);
+dflash_status dflash_o_proj(const void* attn, const void* w_o, int64_t T, int32_t hidden_size,
+                            int32_t in_dim, void* out, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_error_string(lib):
-    assert lib.dflash_abi_version() == 102
+    assert lib.dflash_abi_version() == 103
     assert isinstance(lib.dflash_last_error(), bytes)
 
 
@@ -163,6 +163,46 @@ def test_kv_scatter_validation(lib):
     assert f(B.DFLASH_BF16, None, None, None, 0, 8, 128, None, None, 64, None) == B.DFLASH_OK
     assert f(B.DFLASH_BF16, None, None, None, 4, 8, 128, None, None, 64, None) == B.DFLASH_ERR_INVALID_ARG
     assert f(B.DFLASH_BF16, None, None, None, -1, 8, 128, None, None, 64, None) == B.DFLASH_ERR_INVALID_ARG
+
+
+def test_block_qkv_validation(lib):
+    f = lib.dflash_block_qkv
+    fake = 4096  # never dereferenced: every case fails (or returns) before a launch
+    args = lambda t=4, h=4096, hq=32, hkv=8, dh=128, eps=1e-6, ptr=fake, ws=fake, wsb=1 << 30: (
+        ptr, None, ptr, ptr, t, h, hq, hkv, dh, eps, ptr, ptr, ptr, ws, wsb, None)
+    assert f(*args(t=0, ptr=None, ws=None, wsb=0)) == B.DFLASH_OK          # nothing to do
+    assert f(*args(dh=96)) == B.DFLASH_ERR_UNSUPPORTED
+    assert f(*args(h=100)) == B.DFLASH_ERR_UNSUPPORTED
+    assert f(*args(h=16384)) == B.DFLASH_ERR_UNSUPPORTED
+    assert f(*args(hq=30)) == B.DFLASH_ERR_INVALID_ARG                       # Hq % Hkv
+    assert f(*args(t=-1)) == B.DFLASH_ERR_INVALID_ARG
+    assert f(*args(eps=float("nan"))) == B.DFLASH_ERR_INVALID_ARG
+    assert f(*args(ptr=None)) == B.DFLASH_ERR_INVALID_ARG
+    assert f(*args(ptr=fake + 2)) == B.DFLASH_ERR_INVALID_ARG               # misaligned
+    assert f(*args(ws=None)) == B.DFLASH_ERR_WORKSPACE
+    assert f(*args(ws=fake + 16)) == B.DFLASH_ERR_WORKSPACE                 # not 256-aligned
+    assert f(*args(wsb=16)) == B.DFLASH_ERR_WORKSPACE
+    assert "workspace" in lib.dflash_last_error().decode()
+
+
+def test_o_proj_validation(lib):
+    f = lib.dflash_o_proj
+    fake = 4096
+    assert f(None, None, 0, 4096, 4096, None, None, 0, None) == B.DFLASH_OK
+    assert f(fake, fake, 4, 4000, 4096, fake, fake, 1 << 30, None) == B.DFLASH_ERR_UNSUPPORTED
+    assert f(fake, fake, 4, 4096, 100, fake, fake, 1 << 30, None) == B.DFLASH_ERR_UNSUPPORTED
+    assert f(None, fake, 4, 4096, 4096, fake, fake, 1 << 30, None) == B.DFLASH_ERR_INVALID_ARG
+    assert f(fake, fake, 4, 4096, 4096, fake, None, 0, None) == B.DFLASH_ERR_WORKSPACE
+
+
+def test_layer_workspace_sizes(lib):
+    # small T splits H across workgroups (f32 partials); large T needs only the normed rows
+    small = B.dflash_block_qkv_workspace_size(128, 4096, 32, 8, 128)
+    assert small >= 128 * 4096 * 2 + 2 * 128 * 6144 * 4 and small % 256 == 0
+    assert B.dflash_block_qkv_workspace_size(4096, 4096, 32, 8, 128) == 4096 * 4096 * 2
+    assert B.dflash_o_proj_workspace_size(4096, 4096, 4096) == 0
+    assert B.dflash_o_proj_workspace_size(128, 4096, 4096) >= 2 * 128 * 4096 * 4
+    assert B.dflash_block_qkv_workspace_size(-1, 4096, 32, 8, 128) == 0
 
 
 def test_workspace_sizes(lib):

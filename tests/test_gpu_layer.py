@@ -1,0 +1,190 @@
+"""The draft layer around the attention on the GPU: dflash_block_qkv and
+dflash_o_proj against the oracle, alone and composed with the fused attention.
+
+Bounds (derived from the arithmetic, written per element):
+  * block_qkv: the GPU rounds the normed rows to bf16 (relative error 2^-9,
+    plus up to 2^-9 each from the bf16 residual sum and the f32 rstd it
+    feeds), accumulates in f32 and rounds the output to bf16 (2^-9):
+    |g - o| <= 2^-7 sum_k |n_k W_nk| + 2^-8 |o| + 1e-6.
+  * o_proj: its inputs are exact bf16; f32 accumulation over K <= 8192 terms
+    (<= 2^-11 sum |a W| with the split partial sums) and the bf16 rounding:
+    |g - o| <= 2^-11 sum_k |a_k W_nk| + 2^-8 |o| + 1e-6.
+  * the whole layer: the attention output's own bar (max-abs <= 2e-2,
+    mean-abs <= 2e-3) holds for o, a bf16 activation of the same magnitude
+    (the projection sums 4096 bf16-rounded terms with weights ~N(0, 0.02)).
+"""
+import numpy as np
+import pytest
+import torch
+
+from block_diffusion_draft_dflash_amd import binding as B
+from block_diffusion_draft_dflash_amd.pipeline import LayerPath, bits_to_device, to_host_f64
+from block_diffusion_draft_dflash_amd.workloads import (bf16_bits_to_f32, f32_to_bf16_bits,
+                                                         make_layer_inputs, make_workload)
+
+pytestmark = pytest.mark.gpu
+
+
+def _f(bits):
+    return bf16_bits_to_f32(bits).astype(np.float64)
+
+
+def _check_bound(tag, g, o, absprod, rel_sum, rel_out):
+    bound = rel_sum * absprod + rel_out * np.abs(o) + 1e-6
+    err = np.abs(g - o)
+    worst = float((err / bound).max()) if err.size else 0.0
+    print(f"[{tag}] max abs {err.max() if err.size else 0:.3e} mean abs "
+          f"{err.mean() if err.size else 0:.3e} worst err/bound {worst:.3f}", flush=True)
+    assert worst <= 1.0, f"{tag}: error exceeds the derived bound ({worst:.3f})"
+
+
+QKV_CASES = {
+    # name: (workload overrides, hidden size, residual)
+    "two_reqs_h512": (dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=60), 512, True),
+    "no_residual": (dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=60), 512, False),
+    "ragged_blocks": (dict(name="qwen3_8b_draft", ctx_lens=[0, 5, 130, 0, 77],
+                           blk_lens=[3, 0, 17, 40, 1]), 256, True),
+    "two_row_tiles": (dict(name="qwen3_8b_draft", num_reqs=13, ctx_lo=10, ctx_hi=20), 384, True),
+    "dh64": (dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=10, ctx_hi=20, hq=8, hkv=2, dh=64),
+             256, True),
+    "unsplit_2048_rows": (dict(name="large_decode", num_reqs=128, ctx_lo=4, ctx_hi=8, hq=4, hkv=2),
+                          256, True),
+}
+
+
+def _qkv_case(case):
+    kw, h, use_res = QKV_CASES[case]
+    kw = dict(kw)
+    wl = make_workload(kw.pop("name"), **kw)
+    return wl, make_layer_inputs(wl, h), use_res
+
+
+@pytest.mark.parametrize("case", list(QKV_CASES))
+def test_block_qkv_vs_oracle(case):
+    from oracle import dflash_oracle as O
+    print(f"case block_qkv {case}", flush=True)
+    wl, li, use_res = _qkv_case(case)
+    t, h = wl.total_blk, li.hidden_size
+    dev = "cuda"
+    hid = bits_to_device(li.hidden, dev)
+    res = bits_to_device(li.residual, dev) if use_res else None
+    w_in = torch.from_numpy(li.in_norm_w.astype(np.float32)).to(dev)
+    wq = bits_to_device(li.w_qkv, dev)
+    q = torch.full((t, wl.hq, wl.dh), float("nan"), dtype=torch.bfloat16, device=dev)
+    k = torch.full((t, wl.hkv, wl.dh), float("nan"), dtype=torch.bfloat16, device=dev)
+    v = torch.full((t, wl.hkv, wl.dh), float("nan"), dtype=torch.bfloat16, device=dev)
+    ws = B.alloc_workspace(B.dflash_block_qkv_workspace_size(t, h, wl.hq, wl.hkv, wl.dh), dev)
+    B.dflash_block_qkv(hid, res, w_in, wq, wl.hq, wl.hkv, wl.dh, wl.eps, q, k, v, ws)
+    torch.cuda.synchronize()
+    res_in = _f(li.residual) if use_res else None
+    res_ref, normed = O.residual_rms_norm(_f(li.hidden), res_in, li.in_norm_w, wl.eps)
+    qo, ko, vo = O.block_qkv(normed, _f(li.w_qkv), wl.hq, wl.hkv, wl.dh)
+    absprod = np.abs(normed) @ np.abs(_f(li.w_qkv)).T
+    qd, kd = wl.hq * wl.dh, wl.hkv * wl.dh
+    for name, g, o, ap in (("q", q, qo, absprod[:, :qd]), ("k", k, ko, absprod[:, qd:qd + kd]),
+                           ("v", v, vo, absprod[:, qd + kd:])):
+        _check_bound(f"{case} {name}", to_host_f64(g).reshape(t, -1), o.reshape(t, -1), ap,
+                     2.0 ** -7, 2.0 ** -8)
+    if use_res:
+        # the residual stream is stored as bf16(hidden + residual)
+        want = f32_to_bf16_bits((bf16_bits_to_f32(li.hidden) + bf16_bits_to_f32(li.residual))
+                                .astype(np.float32))
+        got = res.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(got, want), "residual stream != bf16(hidden + residual)"
+
+
+@pytest.mark.parametrize("case", ["two_reqs_h512", "ragged_blocks", "unsplit_2048_rows"])
+def test_o_proj_vs_oracle(case):
+    from oracle import dflash_oracle as O
+    print(f"case o_proj {case}", flush=True)
+    wl, li, _ = _qkv_case(case)
+    t, h = wl.total_blk, li.hidden_size
+    dev = "cuda"
+    rng = np.random.default_rng(77)
+    a_bits = f32_to_bf16_bits(rng.standard_normal((t, wl.hq, wl.dh), dtype=np.float32) * 0.3)
+    attn = bits_to_device(a_bits, dev)
+    w_o = bits_to_device(li.w_o, dev)
+    out = torch.full((t, h), float("nan"), dtype=torch.bfloat16, device=dev)
+    ws = B.alloc_workspace(B.dflash_o_proj_workspace_size(t, h, wl.hq * wl.dh), dev)
+    B.dflash_o_proj(attn, w_o, out, ws)
+    torch.cuda.synchronize()
+    a = _f(a_bits)
+    ref = O.output_projection(a, _f(li.w_o))
+    absprod = np.abs(a.reshape(t, -1)) @ np.abs(_f(li.w_o)).T
+    _check_bound(f"{case} o_proj", to_host_f64(out), ref, absprod, 2.0 ** -11, 2.0 ** -8)
+
+
+LAYER_CASES = {
+    "qwen3_8b_draft_small": (dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=100, ctx_hi=700), 512),
+    "swa_small": (dict(name="swa", num_reqs=2, ctx_len=400, window=128), 256),
+    "empty_ctx": (dict(name="qwen3_8b_draft", ctx_lens=[0, 40], blk_lens=[16, 9]), 256),
+}
+
+
+@pytest.mark.parametrize("case", list(LAYER_CASES))
+def test_layer_vs_oracle(case):
+    from oracle import dflash_oracle as O
+    print(f"case layer {case}", flush=True)
+    kw, h = LAYER_CASES[case]
+    kw = dict(kw)
+    wl = make_workload(kw.pop("name"), **kw)
+    li = make_layer_inputs(wl, h)
+    lp = LayerPath(wl, li)
+    lp.step()
+    torch.cuda.synchronize()
+    _, k_ctx_hat = O.qk_norm_rope(None, wl.k_ctx, None, wl.k_norm_w, wl.ctx_positions, wl.eps,
+                                  wl.theta)
+    o, res, q, k, v, attn = O.draft_layer_attention(
+        _f(li.hidden), _f(li.residual), li.in_norm_w, _f(li.w_qkv), _f(li.w_o), wl.blk_positions,
+        k_ctx_hat, wl.v_ctx, wl.cu_ctx, wl.cu_blk, wl.q_norm_w, wl.k_norm_w, wl.hq, wl.hkv, wl.dh,
+        wl.eps, wl.theta, wl.scale, wl.causal, wl.window)
+    ga = to_host_f64(lp.dp.out)
+    go = to_host_f64(lp.o)
+    ea, eo = np.abs(ga - attn), np.abs(go - o)
+    print(f"[layer {case}] attention max {ea.max():.3e} mean {ea.mean():.3e}; "
+          f"o_proj max {eo.max():.3e} mean {eo.mean():.3e} (max |o| {np.abs(o).max():.2f})",
+          flush=True)
+    assert ea.max() <= 2e-2 and ea.mean() <= 2e-3
+    assert eo.max() <= 2e-2 and eo.mean() <= 2e-3
+
+
+def test_layer_full_qwen3_8b_sampled():
+    # the Qwen3-8B-shaped batch (8 requests, 128 block rows, H = 4096): the
+    # projections checked on sampled rows (rows are independent), the layer
+    # output against the oracle on one request
+    from oracle import dflash_oracle as O
+    print("case layer full qwen3_8b_draft", flush=True)
+    wl = make_workload("qwen3_8b_draft")
+    li = make_layer_inputs(wl, 4096)
+    lp = LayerPath(wl, li)
+    lp.step()
+    torch.cuda.synchronize()
+    rows = np.array([0, 1, 37, 64, 100, 127])
+    _, normed = O.residual_rms_norm(_f(li.hidden[rows]), _f(li.residual[rows]), li.in_norm_w, wl.eps)
+    qo, ko, vo = O.block_qkv(normed, _f(li.w_qkv), wl.hq, wl.hkv, wl.dh)
+    absprod = np.abs(normed) @ np.abs(_f(li.w_qkv)).T
+    qd, kd = wl.hq * wl.dh, wl.hkv * wl.dh
+    for name, g, o, ap in (("q", lp.q, qo, absprod[:, :qd]), ("k", lp.k, ko, absprod[:, qd:qd + kd]),
+                           ("v", lp.v, vo, absprod[:, qd + kd:])):
+        _check_bound(f"full {name}", to_host_f64(g)[rows].reshape(len(rows), -1),
+                     o.reshape(len(rows), -1), ap, 2.0 ** -7, 2.0 ** -8)
+    a = to_host_f64(lp.dp.out)[rows]
+    ref = O.output_projection(a, _f(li.w_o))
+    absprod = np.abs(a.reshape(len(rows), -1)) @ np.abs(_f(li.w_o)).T
+    _check_bound("full o_proj", to_host_f64(lp.o)[rows], ref, absprod, 2.0 ** -11, 2.0 ** -8)
+
+
+def test_layer_repeat_bitwise():
+    print("case layer repeat", flush=True)
+    wl = make_workload("qwen3_8b_draft", num_reqs=3, ctx_lo=100, ctx_hi=300)
+    li = make_layer_inputs(wl, 1024)
+    lp = LayerPath(wl, li)
+    outs = []
+    for _ in range(3):
+        lp.reset_residual()
+        lp.o.zero_()
+        lp.step()
+        torch.cuda.synchronize()
+        outs.append(lp.o.clone())
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
