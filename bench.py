@@ -101,6 +101,71 @@ def cpu_baseline(wl, budget_s: float):
     return el / reps, reps, threads
 
 
+def time_layer(wl, hidden, stream, use_graph, reps=60):
+    """The draft layer around the attention on this batch's block rows:
+    dflash_block_qkv (input norm + merged q/k/v), the fused attention, and
+    dflash_o_proj, each timed with HIP events on the launch stream over
+    weight copies cycled so the last-level cache cannot serve them. Roofline:
+    HBM (the weights are the bytes at these row counts)."""
+    import torch
+    from block_diffusion_draft_dflash_amd.pipeline import LayerPath
+    from block_diffusion_draft_dflash_amd.workloads import make_layer_inputs
+
+    li = make_layer_inputs(wl, hidden)
+    t, n_qkv, in_dim = wl.total_blk, (wl.hq + 2 * wl.hkv) * wl.dh, wl.hq * wl.dh
+    w_bytes = (n_qkv * hidden + hidden * in_dim) * 2
+    copies = max(2, -(-(512 << 20) // max(1, w_bytes)))
+    lps = [LayerPath(wl, li) for _ in range(copies)]
+    for lp in lps:
+        lp.step()
+    torch.cuda.synchronize()
+
+    def run(which):
+        for lp in lps:
+            getattr(lp, which)()
+
+    graphs = {}
+    if use_graph:
+        for which in ("qkv", "o_proj", "step"):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run(which)
+            graphs[which] = g
+        torch.cuda.synchronize()
+
+    def timed(which):
+        go = (lambda: graphs[which].replay()) if use_graph else (lambda: run(which))
+        for _ in range(3):
+            go()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            go()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / (reps * len(lps))
+
+    qkv_us, o_us, step_us = timed("qkv"), timed("o_proj"), timed("step")
+    # algorithmic bytes: block_qkv reads hidden and the residual, writes the
+    # residual and q/k/v, reads the norm weight and W_qkv; o_proj reads the
+    # attention output and W_o and writes its output
+    qkv_bytes = 3 * t * hidden * 2 + hidden * 4 + n_qkv * hidden * 2 + t * n_qkv * 2
+    o_bytes = t * in_dim * 2 + hidden * in_dim * 2 + t * hidden * 2
+    qkv_gbs = qkv_bytes / (qkv_us * 1e-6) / 1e9
+    o_gbs = o_bytes / (o_us * 1e-6) / 1e9
+    return {
+        "hidden": hidden, "weight_copies": copies,
+        "block_qkv": {"us": qkv_us, "bytes": qkv_bytes, "achieved_gbs": qkv_gbs,
+                      "frac": qkv_gbs / HBM_PEAK_GBS, "bound": "hbm"},
+        "o_proj": {"us": o_us, "bytes": o_bytes, "achieved_gbs": o_gbs,
+                   "frac": o_gbs / HBM_PEAK_GBS, "bound": "hbm"},
+        "layer_us": step_us,
+        "layer_note": "block_qkv + dflash_block_attention (fused q/k norm + RoPE) + o_proj",
+    }
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -117,6 +182,9 @@ def main() -> int:
     ap.add_argument("--device-plan", action="store_true",
                     help="leave the work split to the kernels (no host copies of the lengths)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--layer-hidden", type=int, default=4096,
+                    help="hidden size of the draft layer whose projections around the attention "
+                         "(dflash_block_qkv, dflash_o_proj) are also timed (0: skip)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB (3 times) so a "
                          "counter profile of the same run can scale FETCH_SIZE / WRITE_SIZE")
@@ -240,6 +308,10 @@ def main() -> int:
                "frac": ckv_flops / (ckv_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                "flops": ckv_flops, "rows": wl.total_ctx, "hidden": wl.hidden_size}
 
+    layer = None
+    if args.layer_hidden > 0 and wl.dtype == "bf16" and not args.paged:
+        layer = time_layer(wl, args.layer_hidden, stream, use_graph)
+
     cpu = None
     if args.cpu_budget > 0:
         t_cpu, reps, threads = cpu_baseline(wl, args.cpu_budget)
@@ -297,6 +369,7 @@ def main() -> int:
         },
         "cpu_baseline": cpu,
         "context_kv": ckv,
+        "draft_layer": layer,
         "algorithmic": {"attention_bytes": bytes_attn, "attention_flops": flops_attn,
                         "prologue_bytes": bytes_pro},
     }
