@@ -20,4 +20,8 @@ from .dflash_oracle import (  # noqa: F401
     block_qkv,
     output_projection,
     draft_layer_attention,
+    PAD_SLOT,
+    prepare_dflash_inputs,
+    fc_combine,
+    bf16_round,
 )

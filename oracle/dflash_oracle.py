@@ -24,6 +24,10 @@ Sources (pages of the vllm.cpp project):
     ``ForwardPagedBody``: pools of fixed-size pages, a per-request block table
     of page ids; context row p of a request lives at page p // page_size,
     offset p % page_size.
+  * "qwen3_dflash.cpp" page, ``PrepareDflashInputs`` (integer preparation of
+    a propose step: context rows and their slots, rollback of rejected
+    drafts, the anchor + mask block, sample maps, padding) and
+    ``CombineAuxFeatures`` (the multi-tap fc combine).
   * "qwen3_dflash.cpp" page, ``ForwardBlockLogits`` and ``ForwardWithCtxKVDev``
     (the layer around the attention): input_layernorm as the standard
     residual add + RMSNorm, the merged qkv weight applied as one product and
@@ -65,6 +69,10 @@ __all__ = [
     "block_qkv",
     "output_projection",
     "draft_layer_attention",
+    "PAD_SLOT",
+    "prepare_dflash_inputs",
+    "fc_combine",
+    "bf16_round",
 ]
 
 
@@ -332,3 +340,101 @@ def draft_layer_attention(hidden, residual, in_norm_w, w_qkv, w_o, blk_positions
     attn, _, _ = draft_block_attention(q, k, v, blk_positions, k_ctx_hat, v_ctx, cu_ctx, cu_blk,
                                        q_norm_w, k_norm_w, eps, theta, scale, causal, window)
     return output_projection(attn, w_o), res, q, k, v, attn
+
+
+PAD_SLOT = -1  # slot of padding rows ("runner.cpp" page: vLLM's pad slot id)
+
+
+def prepare_dflash_inputs(idx_mapping, target_query_start_loc, target_positions, num_rejected,
+                          num_sampled, last_sampled, next_prefill_tokens, block_table,
+                          num_query_per_req, num_speculative_steps, block_size, max_num_reqs,
+                          max_num_tokens, max_model_len, mask_token_id, sample_from_anchor):
+    """Integer preparation of one DFlash propose step (plain Python loops).
+
+    "qwen3_dflash.cpp" page, ``PrepareDflashInputs`` (the host form of the
+    speculator's input-preparation kernel): per request r, the verified
+    target tokens of the step are its context rows; the last ``num_rejected``
+    of them are rolled back, so the block (the anchor token -- the bonus token
+    last sampled, or the next prefill token for a request that sampled
+    nothing -- followed by mask tokens) starts right after the last kept
+    position. Context and block rows get KV slots from the request's block
+    table (page = position // block_size, clamped to the last page; slot =
+    page id * block_size + position % block_size). The sampled rows of each
+    request are its block rows from offset 0 (``sample_from_anchor``) or 1.
+    Unused tail entries are padded (query_start_loc with the last end,
+    seq_lens 0, sample maps 0 / 0 / -1, query slots PAD_SLOT).
+
+    Returns a dict of int64 numpy arrays.
+    """
+    nreq = len(idx_mapping)
+    nqpr, nspec, bs = int(num_query_per_req), int(num_speculative_steps), int(block_size)
+    tqsl = [int(x) for x in target_query_start_loc]
+    tpos = [int(x) for x in target_positions]
+    bt = np.asarray(block_table, dtype=np.int64).reshape(nreq, -1)
+    stride = bt.shape[1]
+    ntgt = tqsl[nreq]
+    out = {
+        "input_ids": np.zeros(nreq * nqpr, np.int64),
+        "query_positions": np.zeros(nreq * nqpr, np.int64),
+        "query_start_loc": np.zeros(max_num_reqs + 1, np.int64),
+        "seq_lens": np.zeros(max_num_reqs, np.int64),
+        "query_slot_mapping": np.zeros(max_num_tokens, np.int64),
+        "context_positions": np.zeros(ntgt, np.int64),
+        "context_slot_mapping": np.zeros(ntgt, np.int64),
+        "sample_indices": np.zeros(max_num_reqs * nspec, np.int64),
+        "sample_pos": np.zeros(max_num_reqs * nspec, np.int64),
+        "sample_idx_mapping": np.zeros(max_num_reqs * nspec, np.int64),
+    }
+
+    def slot(r, pos):
+        page = min(pos // bs, stride - 1)
+        return int(bt[r, page]) * bs + pos % bs
+
+    first_sample = 0 if sample_from_anchor else 1
+    for r in range(nreq):
+        state = int(idx_mapping[r])
+        start, end = tqsl[r], tqsl[r + 1]
+        kept_end = end - int(num_rejected[r])          # rollback of rejected drafts
+        anchor = int(last_sampled[state]) if int(num_sampled[r]) > 0 else int(next_prefill_tokens[state])
+        last_kept = tpos[kept_end - 1]
+        for t in range(start, end):                    # the step's target rows: context
+            out["context_positions"][t] = tpos[t]
+            out["context_slot_mapping"][t] = slot(r, tpos[t])
+        for off in range(nqpr):                        # the block: anchor + mask tokens
+            pos = last_kept + 1 + off
+            qi = r * nqpr + off
+            out["input_ids"][qi] = anchor if off == 0 else mask_token_id
+            out["query_positions"][qi] = min(pos, max_model_len - 1)
+            out["query_slot_mapping"][qi] = slot(r, pos)
+            if off >= first_sample:
+                si = r * nspec + off - first_sample
+                out["sample_indices"][si] = qi
+                out["sample_pos"][si] = pos + 1 if sample_from_anchor else pos
+                out["sample_idx_mapping"][si] = state
+        out["query_start_loc"][r] = r * nqpr
+        out["seq_lens"][r] = last_kept + 1 + nqpr
+    for i in range(nreq, max_num_reqs + 1):
+        out["query_start_loc"][i] = nreq * nqpr
+    for i in range(nreq * nspec, max_num_reqs * nspec):
+        out["sample_idx_mapping"][i] = -1
+    for i in range(nreq * nqpr, max_num_tokens):
+        out["query_slot_mapping"][i] = PAD_SLOT
+    return out
+
+
+def fc_combine(aux, w_fc):
+    """Multi-tap feature combine: the target's tapped hidden states
+    ``aux [T, H * taps]`` rounded to bf16, times ``w_fc [H, H * taps]`` (as
+    x W^T). "qwen3_dflash.cpp" page, ``CombineAuxFeatures`` (f32 aux cast to
+    bf16, then the fc MatmulBT). ``aux`` is taken as given; the bf16 rounding
+    of f32 inputs is the caller's (see ``bf16_round``)."""
+    return _f64(aux) @ _f64(w_fc).T
+
+
+def bf16_round(x):
+    """Round float values to the nearest bfloat16 (ties to even), as float64:
+    the f32 -> bf16 cast of ``CombineAuxFeatures`` ("qwen3_dflash.cpp" page)."""
+    x32 = np.ascontiguousarray(x, dtype=np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
+    return r.astype(np.uint32).view(np.float32).astype(np.float64)

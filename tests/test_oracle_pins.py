@@ -701,3 +701,110 @@ def test_layer_pins_catch_planted_mistakes(name):
             failed = True
             break
     assert failed, f"no layer pin detects mutant {name}"
+
+
+# ---------------------------------------------------------------- propose-step preparation
+
+def _prep_example(sample_from_anchor=False, max_model_len=100, prep=None):
+    prep = prep or O.prepare_dflash_inputs
+    nqpr = 3
+    return prep(
+        idx_mapping=[1, 0], target_query_start_loc=[0, 3, 4], target_positions=[5, 6, 7, 0],
+        num_rejected=[1, 0], num_sampled=[1, 0], last_sampled=[11, 42], next_prefill_tokens=[17, 99],
+        block_table=[[9, 3, 7], [2, 5, 6]], num_query_per_req=nqpr,
+        num_speculative_steps=nqpr if sample_from_anchor else nqpr - 1, block_size=4,
+        max_num_reqs=3, max_num_tokens=8, max_model_len=max_model_len, mask_token_id=-5,
+        sample_from_anchor=sample_from_anchor)
+
+
+def ppin_hand_example(prep):
+    # worked by hand: request 0 (state 1) keeps positions 5, 6 of its three
+    # verified rows (one rejected), sampled before -> anchor last_sampled[1] = 42
+    # at position 7; request 1 (state 0) has one prefill row at position 0 and
+    # sampled nothing -> anchor next_prefill_tokens[0] = 17 at position 1.
+    o = _prep_example(prep=prep)
+    eq = lambda k, v: np.testing.assert_array_equal(o[k], np.array(v), err_msg=k)
+    eq("context_positions", [5, 6, 7, 0])
+    eq("context_slot_mapping", [3 * 4 + 1, 3 * 4 + 2, 3 * 4 + 3, 2 * 4 + 0])
+    eq("input_ids", [42, -5, -5, 17, -5, -5])
+    eq("query_positions", [7, 8, 9, 1, 2, 3])
+    eq("query_slot_mapping", [3 * 4 + 3, 7 * 4 + 0, 7 * 4 + 1, 2 * 4 + 1, 2 * 4 + 2, 2 * 4 + 3, -1, -1])
+    eq("query_start_loc", [0, 3, 6, 6])
+    eq("seq_lens", [6 + 1 + 3, 0 + 1 + 3, 0])
+    eq("sample_indices", [1, 2, 4, 5, 0, 0])
+    eq("sample_pos", [8, 9, 2, 3, 0, 0])
+    eq("sample_idx_mapping", [1, 1, 0, 0, -1, -1])
+
+
+def ppin_sample_from_anchor_and_clamps(prep):
+    o = _prep_example(sample_from_anchor=True, max_model_len=9, prep=prep)
+    np.testing.assert_array_equal(o["query_positions"], [7, 8, 8, 1, 2, 3])     # min(pos, 8)
+    np.testing.assert_array_equal(o["sample_indices"], [0, 1, 2, 3, 4, 5, 0, 0, 0])
+    np.testing.assert_array_equal(o["sample_pos"], [8, 9, 10, 2, 3, 4, 0, 0, 0])
+    np.testing.assert_array_equal(o["sample_idx_mapping"], [1, 1, 1, 0, 0, 0, -1, -1, -1])
+    # positions past the table's last page use the last page
+    o2 = prep(idx_mapping=[0], target_query_start_loc=[0, 1], target_positions=[14],
+              num_rejected=[0], num_sampled=[1], last_sampled=[3], next_prefill_tokens=[0],
+              block_table=[[4, 8]], num_query_per_req=2, num_speculative_steps=1, block_size=4,
+              max_num_reqs=1, max_num_tokens=2, max_model_len=100, mask_token_id=0,
+              sample_from_anchor=False)
+    np.testing.assert_array_equal(o2["context_slot_mapping"], [8 * 4 + 2])
+    np.testing.assert_array_equal(o2["query_slot_mapping"], [8 * 4 + 3, 8 * 4 + 0])
+
+
+PREP_PINS = [ppin_hand_example, ppin_sample_from_anchor_and_clamps]
+
+
+@pytest.mark.parametrize("pin", PREP_PINS, ids=[p.__name__ for p in PREP_PINS])
+def test_prep_oracle_pin(pin):
+    pin(O.prepare_dflash_inputs)
+
+
+def _prep_mutant(**change):
+    def f(**kw):
+        if change.get("no_rollback"):
+            kw = dict(kw, num_rejected=[0] * len(kw["num_rejected"]))
+        if change.get("anchor_always_last"):
+            kw = dict(kw, num_sampled=[1] * len(kw["num_sampled"]))
+        o = O.prepare_dflash_inputs(**kw)
+        if change.get("no_position_clamp"):
+            o["query_positions"] = O.prepare_dflash_inputs(**dict(kw, max_model_len=1 << 40))["query_positions"]
+        if change.get("sample_pos_shift"):
+            o["sample_pos"] = o["sample_pos"] + (o["sample_idx_mapping"] >= 0)
+        return o
+    return f
+
+
+PREP_MUTANTS = {
+    "no_rollback": dict(no_rollback=True),
+    "anchor_always_last_sampled": dict(anchor_always_last=True),
+    "no_position_clamp": dict(no_position_clamp=True),
+    "sample_pos_off_by_one": dict(sample_pos_shift=True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREP_MUTANTS))
+def test_prep_pins_catch_planted_mistakes(name):
+    f = _prep_mutant(**PREP_MUTANTS[name])
+    failed = False
+    for pin in PREP_PINS:
+        try:
+            pin(f)
+        except AssertionError:
+            failed = True
+            break
+    assert failed, f"no prep pin detects mutant {name}"
+
+
+def test_fc_combine_and_bf16_round_pins():
+    # bf16 rounding against the library's cast; fc against the library's linear
+    x = RNG.standard_normal(1000).astype(np.float32) * np.float32(7.3)
+    x[:4] = [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -0.0, 3.0e38]   # ties to even, sign, large
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), ref)
+    t, h, taps = 5, 8, 3
+    aux = RNG.standard_normal((t, h * taps))
+    w = RNG.standard_normal((h, h * taps))
+    np.testing.assert_allclose(O.fc_combine(aux, w),
+                               torch.nn.functional.linear(torch.from_numpy(aux), torch.from_numpy(w)).numpy(),
+                               rtol=1e-12, atol=1e-12)
