@@ -42,6 +42,9 @@ EXPORTED = (
     "dflash_block_qkv",
     "dflash_o_proj_workspace_size",
     "dflash_o_proj",
+    "dflash_prepare_inputs",
+    "dflash_fc_combine_workspace_size",
+    "dflash_fc_combine",
 )
 
 
@@ -96,6 +99,38 @@ class PagedCtx(ctypes.Structure):
     ]
 
 
+class PrepareParams(ctypes.Structure):
+    """Mirror of ``dflash_prepare_params``."""
+
+    _fields_ = [
+        ("num_reqs", ctypes.c_int32), ("max_num_reqs", ctypes.c_int32),
+        ("max_num_tokens", ctypes.c_int32), ("num_query_per_req", ctypes.c_int32),
+        ("num_speculative_steps", ctypes.c_int32), ("block_size", ctypes.c_int32),
+        ("block_table_stride", ctypes.c_int32), ("max_model_len", ctypes.c_int32),
+        ("mask_token_id", ctypes.c_int32), ("sample_from_anchor", ctypes.c_int32),
+        ("num_states", ctypes.c_int32), ("num_target_tokens", ctypes.c_int64),
+    ]
+
+
+PREP_IN = ("idx_mapping", "target_query_start_loc", "target_positions", "num_rejected",
+           "num_sampled", "last_sampled", "next_prefill_tokens", "block_table")
+PREP_OUT = ("input_ids", "query_positions", "query_start_loc", "seq_lens", "query_slot_mapping",
+            "context_positions", "context_slot_mapping", "sample_indices", "sample_pos",
+            "sample_idx_mapping")
+
+
+class PrepareIn(ctypes.Structure):
+    """Mirror of ``dflash_prepare_inputs_in`` (device pointers)."""
+
+    _fields_ = [(n, ctypes.c_void_p) for n in PREP_IN]
+
+
+class PrepareOut(ctypes.Structure):
+    """Mirror of ``dflash_prepare_inputs_out`` (device pointers)."""
+
+    _fields_ = [(n, ctypes.c_void_p) for n in PREP_OUT]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -147,6 +182,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dflash_o_proj_workspace_size.argtypes = [I64, I32, I32]
     lib.dflash_o_proj.restype = ctypes.c_int
     lib.dflash_o_proj.argtypes = [P, P, I64, I32, I32, P, P, SZ, P]
+    lib.dflash_prepare_inputs.restype = ctypes.c_int
+    lib.dflash_prepare_inputs.argtypes = [ctypes.POINTER(PrepareParams), ctypes.POINTER(PrepareIn),
+                                          ctypes.POINTER(PrepareOut), P]
+    lib.dflash_fc_combine_workspace_size.restype = SZ
+    lib.dflash_fc_combine_workspace_size.argtypes = [I64, I32, I32]
+    lib.dflash_fc_combine.restype = ctypes.c_int
+    lib.dflash_fc_combine.argtypes = [P, P, I64, I32, I32, P, P, SZ, P]
     _lib = lib
     return lib
 
@@ -239,8 +281,10 @@ def dflash_block_attention_workspace_size(p: BlockAttnParams) -> int:
 
 def make_qk_prologue(q_norm_w: torch.Tensor, k_norm_w: torch.Tensor, positions: torch.Tensor,
                      rope_table: torch.Tensor, eps: float) -> QkPrologue:
-    return QkPrologue(_ptr(q_norm_w), _ptr(k_norm_w), _ptr(positions), _ptr(rope_table),
-                      rope_table.shape[0], float(eps))
+    rec = QkPrologue(_ptr(q_norm_w), _ptr(k_norm_w), _ptr(positions), _ptr(rope_table),
+                     rope_table.shape[0], float(eps))
+    rec._keep = (q_norm_w, k_norm_w, positions, rope_table)  # the record holds their pointers
+    return rec
 
 
 def dflash_block_attention(p: BlockAttnParams, cu_ctx_lens: torch.Tensor,
@@ -290,7 +334,9 @@ def make_paged_ctx(block_table: torch.Tensor, num_pages: int, page_size: int = 1
     """``block_table``: device int32 [num_reqs, max_pages_per_req]."""
     if block_table.dtype != torch.int32 or block_table.dim() != 2:
         raise ValueError("block_table must be a 2-D int32 tensor")
-    return PagedCtx(_ptr(block_table), block_table.shape[1], page_size, num_pages)
+    rec = PagedCtx(_ptr(block_table), block_table.shape[1], page_size, num_pages)
+    rec._keep = block_table  # the record holds its pointer
+    return rec
 
 
 def dflash_block_attention_paged_workspace_size(p: BlockAttnParams) -> int:
@@ -357,3 +403,30 @@ def dflash_o_proj(attn: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor,
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(lib.dflash_o_proj(_ptr(attn), _ptr(w_o), t, w_o.shape[0], in_dim, _ptr(out),
                              _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+def dflash_prepare_inputs(params: PrepareParams, inputs: dict, outputs: dict, stream=None) -> None:
+    """``inputs`` / ``outputs``: device tensors keyed by the field names of
+    ``dflash_prepare_inputs_in`` / ``_out`` (int32, or int64 for positions
+    and slots)."""
+    lib = load()
+    pin = PrepareIn(*[_ptr(inputs[n]) for n in PREP_IN])
+    pout = PrepareOut(*[_ptr(outputs[n]) for n in PREP_OUT])
+    _check(lib.dflash_prepare_inputs(ctypes.byref(params), ctypes.byref(pin), ctypes.byref(pout),
+                                     _stream(stream)))
+
+
+def dflash_fc_combine_workspace_size(T: int, hidden_size: int, num_taps: int) -> int:
+    return load().dflash_fc_combine_workspace_size(T, hidden_size, num_taps)
+
+
+def dflash_fc_combine(aux: torch.Tensor, w_fc: torch.Tensor, out: torch.Tensor,
+                      workspace: Optional[torch.Tensor], stream=None) -> None:
+    """``out [T, H] = bf16(aux [T, H * taps]) @ w_fc [H, H * taps]^T``."""
+    lib = load()
+    t = aux.shape[0]
+    h = w_fc.shape[0]
+    taps = w_fc.shape[1] // h
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(lib.dflash_fc_combine(_ptr(aux), _ptr(w_fc), t, h, taps, _ptr(out), _ptr(workspace),
+                                 ws_bytes, _stream(stream)))

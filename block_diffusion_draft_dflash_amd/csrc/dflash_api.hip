@@ -62,7 +62,7 @@ extern "C" {
 
 const char* dflash_last_error(void) { return g_last_error.c_str(); }
 
-int dflash_abi_version(void) { return 103; }
+int dflash_abi_version(void) { return 104; }
 
 dflash_status dflash_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
                                 void* stream) {
@@ -409,6 +409,68 @@ dflash_status dflash_o_proj(const void* attn, const void* w_o, int64_t T, int32_
   return hip_status(dflash::launch_o_proj(attn, w_o, T, hidden_size, in_dim, out, workspace,
                                           kPlanComputeUnits, (hipStream_t)stream),
                     "o_proj launch");
+}
+
+dflash_status dflash_prepare_inputs(const dflash_prepare_params* p,
+                                    const dflash_prepare_inputs_in* in,
+                                    const dflash_prepare_inputs_out* out, void* stream) {
+  if (!p || !in || !out) return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: NULL argument");
+  if (p->num_reqs < 1) return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: num_reqs must be >= 1");
+  if (p->max_num_reqs < p->num_reqs)
+    return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: max_num_reqs < num_reqs");
+  if (p->num_query_per_req < 1)
+    return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: num_query_per_req must be >= 1");
+  if ((int64_t)p->max_num_tokens < (int64_t)p->num_reqs * p->num_query_per_req)
+    return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: max_num_tokens < num_reqs * num_query_per_req");
+  if (p->num_speculative_steps != p->num_query_per_req - (p->sample_from_anchor ? 0 : 1))
+    return fail(DFLASH_ERR_INVALID_ARG,
+                "prepare_inputs: num_speculative_steps must be num_query_per_req - %d",
+                p->sample_from_anchor ? 0 : 1);
+  if (p->block_size < 1 || p->block_table_stride < 1 || p->max_model_len < 1 || p->num_states < 1)
+    return fail(DFLASH_ERR_INVALID_ARG,
+                "prepare_inputs: block_size, block_table_stride, max_model_len and num_states must be >= 1");
+  if (p->num_target_tokens < 1)
+    return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: num_target_tokens must be >= 1");
+  const void* ins[] = {in->idx_mapping, in->target_query_start_loc, in->target_positions,
+                       in->num_rejected, in->num_sampled, in->last_sampled,
+                       in->next_prefill_tokens, in->block_table};
+  for (const void* t : ins)
+    if (!t) return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: NULL input array");
+  const void* outs[] = {out->input_ids, out->query_positions, out->query_start_loc, out->seq_lens,
+                        out->query_slot_mapping, out->context_positions,
+                        out->context_slot_mapping, out->sample_indices, out->sample_pos,
+                        out->sample_idx_mapping};
+  for (const void* t : outs)
+    if (!t) return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: NULL output array");
+  return hip_status(dflash::launch_prepare_inputs(*p, *in, *out, (hipStream_t)stream),
+                    "prepare_inputs launch");
+}
+
+size_t dflash_fc_combine_workspace_size(int64_t T, int32_t hidden_size, int32_t num_taps) {
+  if (T < 0 || hidden_size < 64 || num_taps < 1) return 0;
+  return dflash::fc_combine_workspace_bytes(T, hidden_size, num_taps, kPlanComputeUnits);
+}
+
+dflash_status dflash_fc_combine(const float* aux, const void* w_fc, int64_t T, int32_t hidden_size,
+                                int32_t num_taps, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (T < 0 || T > INT32_MAX) return fail(DFLASH_ERR_INVALID_ARG, "fc_combine: T must be in [0, 2^31)");
+  if (hidden_size < 64 || hidden_size % 64 != 0)
+    return fail(DFLASH_ERR_UNSUPPORTED, "fc_combine: hidden_size must be a positive multiple of 64");
+  if (num_taps < 1 || (int64_t)hidden_size * num_taps > INT32_MAX / 2)
+    return fail(DFLASH_ERR_INVALID_ARG, "fc_combine: num_taps must be >= 1 (and H * taps < 2^30)");
+  if (T == 0) return ok();
+  if (!aux || !w_fc || !out) return fail(DFLASH_ERR_INVALID_ARG, "fc_combine: NULL pointer argument");
+  if (!aligned(aux, 16) || !aligned(w_fc, 16) || !aligned(out, 16))
+    return fail(DFLASH_ERR_INVALID_ARG, "fc_combine: tensors must be 16-byte aligned");
+  const size_t need = dflash::fc_combine_workspace_bytes(T, hidden_size, num_taps, kPlanComputeUnits);
+  if (!workspace) return fail(DFLASH_ERR_WORKSPACE, "fc_combine: workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(workspace, 256)) return fail(DFLASH_ERR_WORKSPACE, "fc_combine: workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(DFLASH_ERR_WORKSPACE, "fc_combine: workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  return hip_status(dflash::launch_fc_combine(aux, w_fc, T, hidden_size, num_taps, out, workspace,
+                                              kPlanComputeUnits, (hipStream_t)stream),
+                    "fc_combine launch");
 }
 
 }  // extern "C"

@@ -55,4 +55,11 @@ size_t o_proj_workspace_bytes(int64_t T, int32_t hidden, int32_t in_dim, int num
 hipError_t launch_o_proj(const void* attn, const void* w_o, int64_t T, int32_t hidden,
                          int32_t in_dim, void* out, void* ws, int num_cus, hipStream_t s);
 
+size_t fc_combine_workspace_bytes(int64_t T, int32_t hidden, int32_t taps, int num_cus);
+hipError_t launch_fc_combine(const float* aux, const void* w_fc, int64_t T, int32_t hidden,
+                             int32_t taps, void* out, void* ws, int num_cus, hipStream_t s);
+
+hipError_t launch_prepare_inputs(const dflash_prepare_params& p, const dflash_prepare_inputs_in& in,
+                                 const dflash_prepare_inputs_out& out, hipStream_t s);
+
 }  // namespace dflash

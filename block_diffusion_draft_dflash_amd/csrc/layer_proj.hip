@@ -395,4 +395,42 @@ hipError_t launch_o_proj(const void* attn, const void* w_o, int64_t T, int32_t h
   return launch_proj((const bf16*)attn, (const bf16*)w_o, T, hidden, in_dim, pl, (float*)ws, o, s);
 }
 
+namespace {
+// f32 -> bf16 (round to nearest even), 8 elements a thread.
+__global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src,
+                                                        bf16* __restrict__ dst, int64_t n8) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 a = reinterpret_cast<const float4*>(src)[2 * i];
+    const float4 b = reinterpret_cast<const float4*>(src)[2 * i + 1];
+    bf16x8 o;
+    o[0] = f2bf(a.x); o[1] = f2bf(a.y); o[2] = f2bf(a.z); o[3] = f2bf(a.w);
+    o[4] = f2bf(b.x); o[5] = f2bf(b.y); o[6] = f2bf(b.z); o[7] = f2bf(b.w);
+    reinterpret_cast<bf16x8*>(dst)[i] = o;
+  }
+}
+}  // namespace
+
+size_t fc_combine_workspace_bytes(int64_t T, int32_t hidden, int32_t taps, int num_cus) {
+  const int32_t k = hidden * taps;
+  return align256((size_t)T * k * sizeof(bf16)) + align256(plan_proj(T, hidden, k, num_cus).part_bytes);
+}
+
+hipError_t launch_fc_combine(const float* aux, const void* w_fc, int64_t T, int32_t hidden,
+                             int32_t taps, void* out, void* ws, int num_cus, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  const int32_t k = hidden * taps;
+  bf16* a = (bf16*)ws;
+  const int64_t n8 = T * k / 8;
+  hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)std::min<int64_t>((n8 + 255) / 256, 4096)),
+                     dim3(256), 0, s, aux, a, n8);
+  const ProjPlan pl = plan_proj(T, hidden, k, num_cus);
+  float* part = (float*)((char*)ws + align256((size_t)T * k * sizeof(bf16)));
+  OutSegs o{};
+  o.ptr[0] = o.ptr[1] = o.ptr[2] = (bf16*)out;
+  o.stride[0] = o.stride[1] = o.stride[2] = hidden;
+  o.begin[0] = 0; o.begin[1] = o.begin[2] = o.begin[3] = hidden;
+  return launch_proj(a, (const bf16*)w_fc, T, hidden, k, pl, part, o, s);
+}
+
 }  // namespace dflash

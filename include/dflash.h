@@ -346,6 +346,86 @@ dflash_status dflash_o_proj(const void* attn, const void* w_o, int64_t T, int32_
                             int32_t in_dim, void* out, void* workspace, size_t workspace_bytes,
                             void* stream);
 
+/*
+ * dflash_prepare_inputs -- integer preparation of one propose step.
+ *
+ * "qwen3_dflash.cpp" page, PrepareDflashInputs. Per request r (state s =
+ * idx_mapping[r]): the step's target rows [start, end) =
+ * target_query_start_loc[r .. r+1] are context rows (their positions and KV
+ * slots are written); the last num_rejected[r] of them are rolled back, so the
+ * block of num_query_per_req rows (the anchor -- last_sampled[s] if
+ * num_sampled[r] > 0, else next_prefill_tokens[s] -- then mask_token_id)
+ * takes positions last_kept + 1 + off (query_positions clamped to
+ * max_model_len - 1; slots from the unclamped position). A slot is
+ * block_table[r][min(pos / block_size, stride - 1)] * block_size +
+ * pos % block_size. Block row off >= (sample_from_anchor ? 0 : 1) is sampled:
+ * sample_indices / sample_pos (pos + 1 when sampling from the anchor, else
+ * pos) / sample_idx_mapping (= s) at r * num_speculative_steps + off - first.
+ * query_start_loc[r] = r * nqpr, seq_lens[r] = last_kept + 1 + nqpr. Tails:
+ * query_start_loc[R .. max_num_reqs] = R * nqpr, seq_lens[R ..) = 0, sample
+ * maps [R * nspec ..) = 0 / 0 / -1, query_slot_mapping[R * nqpr ..
+ * max_num_tokens) = -1 (the pad slot). Integer only: bit-exact.
+ *
+ * Requirements (checked): num_reqs >= 1, max_num_reqs >= num_reqs,
+ * max_num_tokens >= num_reqs * nqpr, nqpr >= 1, num_speculative_steps ==
+ * nqpr - (sample_from_anchor ? 0 : 1), block_size >= 1, block_table_stride >=
+ * 1, max_model_len >= 1, num_states >= 1, num_target_tokens >= 1 (the host
+ * copy of target_query_start_loc[num_reqs]), every pointer non-NULL.
+ * Positions are >= 0. Device metadata is trusted; indices derived from it are
+ * clamped into their buffers.
+ */
+typedef struct {
+  int32_t num_reqs, max_num_reqs, max_num_tokens;
+  int32_t num_query_per_req;      /* 1 + k: the anchor and k mask rows */
+  int32_t num_speculative_steps;  /* sampled rows per request */
+  int32_t block_size, block_table_stride;
+  int32_t max_model_len, mask_token_id, sample_from_anchor;
+  int32_t num_states;             /* entries of last_sampled / next_prefill_tokens */
+  int64_t num_target_tokens;
+} dflash_prepare_params;
+
+typedef struct { /* device inputs */
+  const int32_t* idx_mapping;             /* [num_reqs] */
+  const int32_t* target_query_start_loc;  /* [num_reqs + 1] */
+  const int64_t* target_positions;        /* [num_target_tokens] */
+  const int32_t* num_rejected;            /* [num_reqs] */
+  const int32_t* num_sampled;             /* [num_reqs] */
+  const int32_t* last_sampled;            /* [num_states] */
+  const int32_t* next_prefill_tokens;     /* [num_states] */
+  const int32_t* block_table;             /* [num_reqs][block_table_stride] */
+} dflash_prepare_inputs_in;
+
+typedef struct { /* device outputs */
+  int32_t* input_ids;             /* [num_reqs * nqpr] */
+  int64_t* query_positions;       /* [num_reqs * nqpr] */
+  int32_t* query_start_loc;       /* [max_num_reqs + 1] */
+  int32_t* seq_lens;              /* [max_num_reqs] */
+  int64_t* query_slot_mapping;    /* [max_num_tokens] */
+  int64_t* context_positions;     /* [num_target_tokens] */
+  int64_t* context_slot_mapping;  /* [num_target_tokens] */
+  int32_t* sample_indices;        /* [max_num_reqs * nspec] */
+  int64_t* sample_pos;            /* [max_num_reqs * nspec] */
+  int32_t* sample_idx_mapping;    /* [max_num_reqs * nspec] */
+} dflash_prepare_inputs_out;
+
+dflash_status dflash_prepare_inputs(const dflash_prepare_params* p,
+                                    const dflash_prepare_inputs_in* in,
+                                    const dflash_prepare_inputs_out* out, void* stream);
+
+/*
+ * dflash_fc_combine -- the multi-tap feature combine (bf16 product).
+ *
+ * out = bf16(aux) w_fc^T: the target's tapped hidden states aux [T, H * taps]
+ * (f32) rounded to bf16, times the fc weight w_fc [H, H * taps] (bf16,
+ * row-major), out [T, H] bf16. "qwen3_dflash.cpp" page, CombineAuxFeatures.
+ * workspace: 256-byte aligned, >= dflash_fc_combine_workspace_size bytes.
+ * Requirements: H % 64 == 0, num_taps >= 1; tensors 16-byte aligned; T may be 0.
+ */
+size_t dflash_fc_combine_workspace_size(int64_t T, int32_t hidden_size, int32_t num_taps);
+dflash_status dflash_fc_combine(const float* aux, const void* w_fc, int64_t T, int32_t hidden_size,
+                                int32_t num_taps, void* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

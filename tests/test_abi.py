@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_error_string(lib):
-    assert lib.dflash_abi_version() == 103
+    assert lib.dflash_abi_version() == 104
     assert isinstance(lib.dflash_last_error(), bytes)
 
 
@@ -237,3 +237,34 @@ def _load_fresh(path):
         return B.load(path)
     finally:
         B._lib = saved
+
+
+def test_prepare_inputs_validation(lib):
+    import ctypes
+    good = dict(num_reqs=2, max_num_reqs=3, max_num_tokens=8, num_query_per_req=3,
+                num_speculative_steps=2, block_size=16, block_table_stride=4, max_model_len=100,
+                mask_token_id=5, sample_from_anchor=0, num_states=2, num_target_tokens=4)
+    fake = ctypes.c_void_p(4096)
+    pin = B.PrepareIn(*([fake] * len(B.PREP_IN)))
+    pout = B.PrepareOut(*([fake] * len(B.PREP_OUT)))
+    f = lambda **ch: lib.dflash_prepare_inputs(ctypes.byref(B.PrepareParams(**dict(good, **ch))),
+                                               ctypes.byref(pin), ctypes.byref(pout), None)
+    assert f(num_reqs=0) == B.DFLASH_ERR_INVALID_ARG
+    assert f(max_num_reqs=1) == B.DFLASH_ERR_INVALID_ARG
+    assert f(max_num_tokens=5) == B.DFLASH_ERR_INVALID_ARG
+    assert f(num_speculative_steps=3) == B.DFLASH_ERR_INVALID_ARG        # must be nqpr - 1 here
+    assert f(block_size=0) == B.DFLASH_ERR_INVALID_ARG
+    assert f(num_target_tokens=0) == B.DFLASH_ERR_INVALID_ARG
+    nul = B.PrepareIn(*([fake] * (len(B.PREP_IN) - 1) + [None]))
+    assert lib.dflash_prepare_inputs(ctypes.byref(B.PrepareParams(**good)), ctypes.byref(nul),
+                                     ctypes.byref(pout), None) == B.DFLASH_ERR_INVALID_ARG
+
+
+def test_fc_combine_validation(lib):
+    f = lib.dflash_fc_combine
+    fake = 4096
+    assert f(None, None, 0, 4096, 5, None, None, 0, None) == B.DFLASH_OK
+    assert f(fake, fake, 4, 100, 5, fake, fake, 1 << 30, None) == B.DFLASH_ERR_UNSUPPORTED
+    assert f(fake, fake, 4, 4096, 0, fake, fake, 1 << 30, None) == B.DFLASH_ERR_INVALID_ARG
+    assert f(fake, fake, 4, 4096, 5, fake, None, 0, None) == B.DFLASH_ERR_WORKSPACE
+    assert B.dflash_fc_combine_workspace_size(128, 4096, 5) >= 128 * 4096 * 5 * 2
