@@ -116,7 +116,7 @@ PREP_IN = ("idx_mapping", "target_query_start_loc", "target_positions", "num_rej
            "num_sampled", "last_sampled", "next_prefill_tokens", "block_table")
 PREP_OUT = ("input_ids", "query_positions", "query_start_loc", "seq_lens", "query_slot_mapping",
             "context_positions", "context_slot_mapping", "sample_indices", "sample_pos",
-            "sample_idx_mapping")
+            "sample_idx_mapping", "ctx_cu")
 
 
 class PrepareIn(ctypes.Structure):
@@ -406,9 +406,8 @@ def dflash_o_proj(attn: torch.Tensor, w_o: torch.Tensor, out: torch.Tensor,
 
 
 def dflash_prepare_inputs(params: PrepareParams, inputs: dict, outputs: dict, stream=None) -> None:
-    """``inputs`` / ``outputs``: device tensors keyed by the field names of
-    ``dflash_prepare_inputs_in`` / ``_out`` (int32, or int64 for positions
-    and slots)."""
+    """``inputs`` / ``outputs``: device int32 tensors keyed by the field names
+    of ``dflash_prepare_inputs_in`` / ``_out``."""
     lib = load()
     pin = PrepareIn(*[_ptr(inputs[n]) for n in PREP_IN])
     pout = PrepareOut(*[_ptr(outputs[n]) for n in PREP_OUT])

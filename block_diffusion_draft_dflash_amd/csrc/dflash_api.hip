@@ -439,7 +439,7 @@ dflash_status dflash_prepare_inputs(const dflash_prepare_params* p,
   const void* outs[] = {out->input_ids, out->query_positions, out->query_start_loc, out->seq_lens,
                         out->query_slot_mapping, out->context_positions,
                         out->context_slot_mapping, out->sample_indices, out->sample_pos,
-                        out->sample_idx_mapping};
+                        out->sample_idx_mapping, out->ctx_cu};
   for (const void* t : outs)
     if (!t) return fail(DFLASH_ERR_INVALID_ARG, "prepare_inputs: NULL output array");
   return hip_status(dflash::launch_prepare_inputs(*p, *in, *out, (hipStream_t)stream),

@@ -24,7 +24,18 @@ __device__ __forceinline__ int64_t clamp64(int64_t x, int64_t lo, int64_t hi) {
   return x < lo ? lo : (x > hi ? hi : x);
 }
 
-// Workgroup r < num_reqs: request r. Workgroup num_reqs: the padded tails.
+// The last kept position of request r (index clamped into the target rows).
+__device__ __forceinline__ int64_t last_kept_pos(const dflash_prepare_params& p,
+                                                 const dflash_prepare_inputs_in& in, int32_t r) {
+  const int64_t ntgt = p.num_target_tokens;
+  const int64_t start = clamp64(in.target_query_start_loc[r], 0, ntgt);
+  const int64_t end = clamp64(in.target_query_start_loc[r + 1], start, ntgt);
+  const int64_t kept_end = end - in.num_rejected[r];
+  return in.target_positions[clamp64(kept_end - 1, 0, ntgt - 1)];
+}
+
+// Workgroup r < num_reqs: request r. Workgroup num_reqs: the cumulative
+// kept-context lengths and the padded tails.
 __global__ __launch_bounds__(PT) void prepare_inputs_kernel(dflash_prepare_params p,
                                                             dflash_prepare_inputs_in in,
                                                             dflash_prepare_inputs_out out) {
@@ -33,6 +44,16 @@ __global__ __launch_bounds__(PT) void prepare_inputs_kernel(dflash_prepare_param
   const int32_t nqpr = p.num_query_per_req, nspec = p.num_speculative_steps;
   const int32_t R = p.num_reqs;
   if (r == R) {
+    if (tid == 0) {
+      // running sum over the requests, in order (one thread: R is small)
+      int32_t acc = 0;
+      out.ctx_cu[0] = 0;
+      for (int32_t i = 0; i < R; ++i) {
+        acc += (int32_t)(last_kept_pos(p, in, i) + 1);
+        out.ctx_cu[i + 1] = acc;
+      }
+      for (int32_t i = R + 1; i <= p.max_num_reqs; ++i) out.ctx_cu[i] = acc;
+    }
     for (int64_t i = R + tid; i <= p.max_num_reqs; i += PT) out.query_start_loc[i] = R * nqpr;
     for (int64_t i = R + tid; i < p.max_num_reqs; i += PT) out.seq_lens[i] = 0;
     for (int64_t i = (int64_t)R * nspec + tid; i < (int64_t)p.max_num_reqs * nspec; i += PT) {
@@ -50,18 +71,17 @@ __global__ __launch_bounds__(PT) void prepare_inputs_kernel(dflash_prepare_param
   const int32_t state = (int32_t)clamp64(in.idx_mapping[r], 0, p.num_states - 1);
   const int64_t start = clamp64(in.target_query_start_loc[r], 0, ntgt);
   const int64_t end = clamp64(in.target_query_start_loc[r + 1], start, ntgt);
-  const int64_t kept_end = end - in.num_rejected[r];
-  const int64_t last_kept = in.target_positions[clamp64(kept_end - 1, 0, ntgt - 1)];
+  const int64_t last_kept = last_kept_pos(p, in, r);
   const int32_t anchor = in.num_sampled[r] > 0 ? in.last_sampled[state] : in.next_prefill_tokens[state];
   const int32_t* bt = in.block_table + (int64_t)r * p.block_table_stride;
   const int64_t bs = p.block_size;
-  auto slot = [&](int64_t pos) -> int64_t {
+  auto slot = [&](int64_t pos) -> int32_t {
     const int64_t page = clamp64(pos / bs, 0, p.block_table_stride - 1);
-    return (int64_t)bt[page] * bs + pos % bs;
+    return (int32_t)((int64_t)bt[page] * bs + pos % bs);
   };
   for (int64_t t = start + tid; t < end; t += PT) {
     const int64_t pos = in.target_positions[t];
-    out.context_positions[t] = pos;
+    out.context_positions[t] = (int32_t)pos;
     out.context_slot_mapping[t] = slot(pos);
   }
   const int32_t first_sample = p.sample_from_anchor ? 0 : 1;
@@ -69,12 +89,12 @@ __global__ __launch_bounds__(PT) void prepare_inputs_kernel(dflash_prepare_param
     const int64_t pos = last_kept + 1 + off;
     const int64_t qi = (int64_t)r * nqpr + off;
     out.input_ids[qi] = off == 0 ? anchor : p.mask_token_id;
-    out.query_positions[qi] = std::min<int64_t>(pos, (int64_t)p.max_model_len - 1);
+    out.query_positions[qi] = (int32_t)std::min<int64_t>(pos, (int64_t)p.max_model_len - 1);
     out.query_slot_mapping[qi] = slot(pos);
     if (off >= first_sample) {
       const int64_t si = (int64_t)r * nspec + (off - first_sample);
       out.sample_indices[si] = (int32_t)qi;
-      out.sample_pos[si] = p.sample_from_anchor ? pos + 1 : pos;
+      out.sample_pos[si] = (int32_t)(p.sample_from_anchor ? pos + 1 : pos);
       out.sample_idx_mapping[si] = state;
     }
   }

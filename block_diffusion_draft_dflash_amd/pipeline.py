@@ -10,7 +10,8 @@ through the C ABI:
   ``dflash_block_attention`` over [context; block]; or the one fused call;
 * the draft layer around it (:class:`LayerPath`): ``dflash_block_qkv`` (input
   norm and merged q/k/v projection of the block rows), the fused attention,
-  ``dflash_o_proj``.
+  ``dflash_o_proj``;
+* a whole propose step (:class:`DraftStep`), capturable into a HIP graph.
 
 By default the host copies of the cumulative lengths go with the attention
 parameters (the work split is then planned on the host); ``host_lengths=False``
@@ -26,7 +27,7 @@ import numpy as np
 import torch
 
 from . import binding as B
-from .workloads import LayerInputs, Workload, f32_to_bf16_bits
+from .workloads import LayerInputs, Workload, bf16_bits_to_f32, f32_to_bf16_bits
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -250,3 +251,110 @@ class LayerPath:
         self.qkv()
         self.attention()
         self.o_proj()
+
+
+class DraftStep:
+    """One propose step of a draft layer, every stage a library call on one
+    stream with fixed buffers, so the whole step can be captured into a HIP
+    graph and replayed with its inputs refreshed in place:
+
+      dflash_prepare_inputs -> dflash_fc_combine (the target's tapped features
+      of the verified rows) -> dflash_context_kv (their K/V at the prepared
+      context positions) -> dflash_kv_scatter (into the paged store at the
+      prepared slots) -> dflash_block_qkv (the block rows' hidden states) ->
+      dflash_block_attention_paged (fused q/k norm + RoPE at the prepared block
+      positions; the work split planned on the device from ctx_cu and
+      query_start_loc) -> dflash_o_proj.
+
+    Each request verifies ``rows_per_req`` rows per step; the block rows'
+    hidden states (the embedding of the anchor + mask tokens, outside this
+    library) are a fixed synthetic input."""
+
+    def __init__(self, num_reqs: int, nqpr: int, rows_per_req: int, hidden: int = 256,
+                 taps: int = 3, hq: int = 4, hkv: int = 2, dh: int = 128, pages_per_req: int = 16,
+                 seed: int = 0, device: str = "cuda", eps: float = 1e-6, theta: float = 1e6):
+        rng = np.random.default_rng(seed)
+        self.r, self.nqpr, self.rows = num_reqs, nqpr, rows_per_req
+        self.h, self.taps, self.hq, self.hkv, self.dh = hidden, taps, hq, hkv, dh
+        self.eps = eps
+        dev = device
+        i32 = lambda a: torch.tensor(np.asarray(a, dtype=np.int32), device=dev)
+        bits = lambda shape, s: bits_to_device(f32_to_bf16_bits(
+            rng.standard_normal(shape, dtype=np.float32) * np.float32(s)), dev)
+        f32w = lambda n: torch.from_numpy(bf16_bits_to_f32(f32_to_bf16_bits(
+            rng.uniform(0.5, 1.5, n).astype(np.float32)))).to(dev)
+        page = 16
+        self.pages = num_reqs * pages_per_req + 3
+        bt = rng.permutation(self.pages)[:num_reqs * pages_per_req].reshape(num_reqs, pages_per_req)
+        self.block_table = i32(bt)
+        ntgt = num_reqs * rows_per_req
+        # inputs refreshed in place every step
+        self.ins = {n: torch.zeros(ntgt if n == "target_positions" else
+                                   (num_reqs + 1 if n == "target_query_start_loc" else num_reqs),
+                                   dtype=torch.int32, device=dev)
+                    for n in B.PREP_IN if n != "block_table"}
+        self.ins["block_table"] = self.block_table
+        self.ins["target_query_start_loc"].copy_(torch.arange(num_reqs + 1, dtype=torch.int32) * rows_per_req)
+        self.ins["idx_mapping"].copy_(torch.arange(num_reqs, dtype=torch.int32))
+        self.aux = torch.zeros((ntgt, hidden * taps), dtype=torch.float32, device=dev)
+        sizes = dict(input_ids=num_reqs * nqpr, query_positions=num_reqs * nqpr,
+                     query_start_loc=num_reqs + 1, seq_lens=num_reqs,
+                     query_slot_mapping=num_reqs * nqpr, context_positions=ntgt,
+                     context_slot_mapping=ntgt, sample_indices=num_reqs * (nqpr - 1),
+                     sample_pos=num_reqs * (nqpr - 1), sample_idx_mapping=num_reqs * (nqpr - 1),
+                     ctx_cu=num_reqs + 1)
+        self.outs = {n: torch.zeros(sizes[n], dtype=torch.int32, device=dev) for n in B.PREP_OUT}
+        self.prep = B.PrepareParams(num_reqs, num_reqs, num_reqs * nqpr, nqpr, nqpr - 1, page,
+                                    pages_per_req, 1 << 20, 7, 0, num_reqs, ntgt)
+        # weights (synthetic, bf16) and norm weights
+        self.w_fc = bits((hidden, hidden * taps), 0.05)
+        self.hnw, self.knw, self.qnw, self.in_norm_w = f32w(hidden), f32w(dh), f32w(dh), f32w(hidden)
+        self.w_k, self.w_v = bits((hkv * dh, hidden), 0.05), bits((hkv * dh, hidden), 0.05)
+        self.w_qkv = bits(((hq + 2 * hkv) * dh, hidden), 0.05)
+        self.w_o = bits((hidden, hq * dh), 0.05)
+        self.blk_hidden = bits((num_reqs * nqpr, hidden), 1.0)
+        self.rope = torch.empty((1 << 14, dh // 2, 2), dtype=torch.float32, device=dev)
+        B.dflash_rope_table(self.rope, 1 << 14, dh, theta)
+        bf = torch.bfloat16
+        self.k_pool = torch.zeros((self.pages, page, hkv, dh), dtype=bf, device=dev)
+        self.v_pool = torch.zeros_like(self.k_pool)
+        self.comb = torch.empty((ntgt, hidden), dtype=bf, device=dev)
+        self.k_new = torch.empty((ntgt, hkv, dh), dtype=bf, device=dev)
+        self.v_new = torch.empty_like(self.k_new)
+        t = num_reqs * nqpr
+        self.q = torch.empty((t, hq, dh), dtype=bf, device=dev)
+        self.kb = torch.empty((t, hkv, dh), dtype=bf, device=dev)
+        self.vb = torch.empty_like(self.kb)
+        self.attn = torch.empty_like(self.q)
+        self.o = torch.empty((t, hidden), dtype=bf, device=dev)
+        self.params = B.make_block_attn_params(num_reqs, hq, hkv, dh, B.DFLASH_BF16,
+                                               num_reqs * pages_per_req * page, t, nqpr, dh ** -0.5)
+        self.pg = B.make_paged_ctx(self.block_table, self.pages)
+        self.pro = B.make_qk_prologue(self.qnw, self.knw, self.outs["query_positions"], self.rope, eps)
+        self.ws_fc = B.alloc_workspace(B.dflash_fc_combine_workspace_size(ntgt, hidden, taps), dev)
+        self.ws_ckv = B.alloc_workspace(B.dflash_context_kv_workspace_size(ntgt, hidden, hkv, dh), dev)
+        self.ws_qkv = B.alloc_workspace(B.dflash_block_qkv_workspace_size(t, hidden, hq, hkv, dh), dev)
+        self.ws_attn = B.alloc_workspace(B.dflash_block_attention_paged_workspace_size(self.params), dev)
+        self.ws_o = B.alloc_workspace(B.dflash_o_proj_workspace_size(t, hidden, hq * dh), dev)
+
+    def set_step(self, positions, rejected, sampled, last_sampled, aux) -> None:
+        """Refresh the step's inputs in place (host arrays)."""
+        self.ins["target_positions"].copy_(torch.from_numpy(np.asarray(positions, np.int32)))
+        self.ins["num_rejected"].copy_(torch.from_numpy(np.asarray(rejected, np.int32)))
+        self.ins["num_sampled"].copy_(torch.from_numpy(np.asarray(sampled, np.int32)))
+        self.ins["last_sampled"].copy_(torch.from_numpy(np.asarray(last_sampled, np.int32)))
+        self.aux.copy_(torch.from_numpy(np.ascontiguousarray(aux, np.float32)))
+
+    def run(self) -> None:
+        o = self.outs
+        B.dflash_prepare_inputs(self.prep, self.ins, o)
+        B.dflash_fc_combine(self.aux, self.w_fc, self.comb, self.ws_fc)
+        B.dflash_context_kv(self.comb, self.hnw, self.w_k, self.w_v, self.knw, o["context_positions"],
+                            self.hkv, self.dh, self.eps, self.rope, self.k_new, self.v_new, self.ws_ckv)
+        B.dflash_kv_scatter(self.k_new, self.v_new, o["context_slot_mapping"], self.k_pool, self.v_pool)
+        B.dflash_block_qkv(self.blk_hidden, None, self.in_norm_w, self.w_qkv, self.hq, self.hkv,
+                           self.dh, self.eps, self.q, self.kb, self.vb, self.ws_qkv)
+        B.dflash_block_attention_paged(self.params, self.pg, o["ctx_cu"], o["query_start_loc"], self.q,
+                                       self.kb, self.vb, self.k_pool, self.v_pool, self.attn,
+                                       self.ws_attn, prologue=self.pro)
+        B.dflash_o_proj(self.attn, self.w_o, self.o, self.ws_o)

@@ -361,10 +361,15 @@ dflash_status dflash_o_proj(const void* attn, const void* w_o, int64_t T, int32_
  * pos % block_size. Block row off >= (sample_from_anchor ? 0 : 1) is sampled:
  * sample_indices / sample_pos (pos + 1 when sampling from the anchor, else
  * pos) / sample_idx_mapping (= s) at r * num_speculative_steps + off - first.
- * query_start_loc[r] = r * nqpr, seq_lens[r] = last_kept + 1 + nqpr. Tails:
- * query_start_loc[R .. max_num_reqs] = R * nqpr, seq_lens[R ..) = 0, sample
- * maps [R * nspec ..) = 0 / 0 / -1, query_slot_mapping[R * nqpr ..
- * max_num_tokens) = -1 (the pad slot). Integer only: bit-exact.
+ * query_start_loc[r] = r * nqpr, seq_lens[r] = last_kept + 1 + nqpr, and the
+ * cumulative kept-context lengths ctx_cu[r + 1] = ctx_cu[r] + last_kept + 1
+ * (ctx_cu[0] = 0; the runner page's ctx_cu, the attention's cu_ctx_lens, with
+ * query_start_loc as its cu_blk_lens). Tails: query_start_loc[R ..
+ * max_num_reqs] = R * nqpr, ctx_cu[R + 1 .. max_num_reqs] = ctx_cu[R],
+ * seq_lens[R ..) = 0, sample maps [R * nspec ..) = 0 / 0 / -1,
+ * query_slot_mapping[R * nqpr .. max_num_tokens) = -1 (the pad slot).
+ * Positions and slots are int32 (as every other call of this library takes
+ * them); integer only: bit-exact.
  *
  * Requirements (checked): num_reqs >= 1, max_num_reqs >= num_reqs,
  * max_num_tokens >= num_reqs * nqpr, nqpr >= 1, num_speculative_steps ==
@@ -387,7 +392,7 @@ typedef struct {
 typedef struct { /* device inputs */
   const int32_t* idx_mapping;             /* [num_reqs] */
   const int32_t* target_query_start_loc;  /* [num_reqs + 1] */
-  const int64_t* target_positions;        /* [num_target_tokens] */
+  const int32_t* target_positions;        /* [num_target_tokens] */
   const int32_t* num_rejected;            /* [num_reqs] */
   const int32_t* num_sampled;             /* [num_reqs] */
   const int32_t* last_sampled;            /* [num_states] */
@@ -397,15 +402,16 @@ typedef struct { /* device inputs */
 
 typedef struct { /* device outputs */
   int32_t* input_ids;             /* [num_reqs * nqpr] */
-  int64_t* query_positions;       /* [num_reqs * nqpr] */
+  int32_t* query_positions;       /* [num_reqs * nqpr] */
   int32_t* query_start_loc;       /* [max_num_reqs + 1] */
   int32_t* seq_lens;              /* [max_num_reqs] */
-  int64_t* query_slot_mapping;    /* [max_num_tokens] */
-  int64_t* context_positions;     /* [num_target_tokens] */
-  int64_t* context_slot_mapping;  /* [num_target_tokens] */
+  int32_t* query_slot_mapping;    /* [max_num_tokens] */
+  int32_t* context_positions;     /* [num_target_tokens] */
+  int32_t* context_slot_mapping;  /* [num_target_tokens] */
   int32_t* sample_indices;        /* [max_num_reqs * nspec] */
-  int64_t* sample_pos;            /* [max_num_reqs * nspec] */
+  int32_t* sample_pos;            /* [max_num_reqs * nspec] */
   int32_t* sample_idx_mapping;    /* [max_num_reqs * nspec] */
+  int32_t* ctx_cu;                /* [max_num_reqs + 1] */
 } dflash_prepare_inputs_out;
 
 dflash_status dflash_prepare_inputs(const dflash_prepare_params* p,

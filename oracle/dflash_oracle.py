@@ -362,7 +362,10 @@ def prepare_dflash_inputs(idx_mapping, target_query_start_loc, target_positions,
     page id * block_size + position % block_size). The sampled rows of each
     request are its block rows from offset 0 (``sample_from_anchor``) or 1.
     Unused tail entries are padded (query_start_loc with the last end,
-    seq_lens 0, sample maps 0 / 0 / -1, query slots PAD_SLOT).
+    seq_lens 0, sample maps 0 / 0 / -1, query slots PAD_SLOT). ``ctx_cu`` is the
+    running sum of the kept context lengths (last kept position + 1) over the
+    requests -- the cumulative context offsets the "runner.cpp" page hands
+    the block forward (``ctx_cu``) -- padded with its total.
 
     Returns a dict of int64 numpy arrays.
     """
@@ -384,6 +387,7 @@ def prepare_dflash_inputs(idx_mapping, target_query_start_loc, target_positions,
         "sample_indices": np.zeros(max_num_reqs * nspec, np.int64),
         "sample_pos": np.zeros(max_num_reqs * nspec, np.int64),
         "sample_idx_mapping": np.zeros(max_num_reqs * nspec, np.int64),
+        "ctx_cu": np.zeros(max_num_reqs + 1, np.int64),
     }
 
     def slot(r, pos):
@@ -413,8 +417,10 @@ def prepare_dflash_inputs(idx_mapping, target_query_start_loc, target_positions,
                 out["sample_idx_mapping"][si] = state
         out["query_start_loc"][r] = r * nqpr
         out["seq_lens"][r] = last_kept + 1 + nqpr
+        out["ctx_cu"][r + 1] = out["ctx_cu"][r] + last_kept + 1
     for i in range(nreq, max_num_reqs + 1):
         out["query_start_loc"][i] = nreq * nqpr
+        out["ctx_cu"][i] = out["ctx_cu"][nreq]
     for i in range(nreq * nspec, max_num_reqs * nspec):
         out["sample_idx_mapping"][i] = -1
     for i in range(nreq * nqpr, max_num_tokens):

@@ -19,9 +19,6 @@ from block_diffusion_draft_dflash_amd.workloads import bf16_bits_to_f32, f32_to_
 
 pytestmark = pytest.mark.gpu
 
-I32 = ("idx_mapping", "target_query_start_loc", "num_rejected", "num_sampled", "last_sampled",
-       "next_prefill_tokens", "block_table", "input_ids", "query_start_loc", "seq_lens",
-       "sample_indices", "sample_idx_mapping")
 
 
 def _run_prep(batch, sentinel=-777):
@@ -32,17 +29,16 @@ def _run_prep(batch, sentinel=-777):
     nqpr, nspec = batch["num_query_per_req"], batch["num_speculative_steps"]
     ntgt = int(batch["target_query_start_loc"][-1])
     bt = np.asarray(batch["block_table"], dtype=np.int64).reshape(r, -1)
-    t = lambda a, name: torch.tensor(np.asarray(a, dtype=np.int32 if name in I32 else np.int64),
-                                     device=dev)
+    t = lambda a, name: torch.tensor(np.asarray(a, dtype=np.int32), device=dev)
     ins = {n: t(batch[n] if n != "block_table" else bt, n) for n in B.PREP_IN}
     sizes = dict(input_ids=r * nqpr, query_positions=r * nqpr,
                  query_start_loc=batch["max_num_reqs"] + 1, seq_lens=batch["max_num_reqs"],
                  query_slot_mapping=batch["max_num_tokens"], context_positions=ntgt,
                  context_slot_mapping=ntgt, sample_indices=batch["max_num_reqs"] * nspec,
                  sample_pos=batch["max_num_reqs"] * nspec,
-                 sample_idx_mapping=batch["max_num_reqs"] * nspec)
-    outs = {n: torch.full((sizes[n],), sentinel, dtype=torch.int32 if n in I32 else torch.int64,
-                          device=dev) for n in B.PREP_OUT}
+                 sample_idx_mapping=batch["max_num_reqs"] * nspec,
+                 ctx_cu=batch["max_num_reqs"] + 1)
+    outs = {n: torch.full((sizes[n],), sentinel, dtype=torch.int32, device=dev) for n in B.PREP_OUT}
     p = B.PrepareParams(r, batch["max_num_reqs"], batch["max_num_tokens"], nqpr, nspec,
                         batch["block_size"], bt.shape[1], batch["max_model_len"],
                         batch["mask_token_id"], int(batch["sample_from_anchor"]),

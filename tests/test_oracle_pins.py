@@ -734,6 +734,7 @@ def ppin_hand_example(prep):
     eq("sample_indices", [1, 2, 4, 5, 0, 0])
     eq("sample_pos", [8, 9, 2, 3, 0, 0])
     eq("sample_idx_mapping", [1, 1, 0, 0, -1, -1])
+    eq("ctx_cu", [0, 7, 8, 8])                         # kept context rows: 0..6 and 0
 
 
 def ppin_sample_from_anchor_and_clamps(prep):
