@@ -166,6 +166,54 @@ def time_layer(wl, hidden, stream, use_graph, reps=60):
     }
 
 
+def time_draft_step(wl, hidden, taps, stream, reps=50):
+    """A whole propose step of one draft layer on this batch's shape, replayed
+    from one HIP graph: the integer preparation, fc combine of the verified
+    rows' tapped features, their context K/V appended to a paged store,
+    block q/k/v, the paged attention (work split planned on the device) and
+    o_proj. Each request verifies one block of rows on top of its context."""
+    import numpy as np
+    import torch
+    from block_diffusion_draft_dflash_amd.pipeline import DraftStep
+
+    nqpr = int(wl.blk_lens.max())
+    rows = nqpr
+    pages = (int(wl.ctx_lens.max()) + rows + 15) // 16 + 1
+    ds = DraftStep(wl.num_reqs, nqpr, rows, hidden=hidden, taps=taps, hq=wl.hq, hkv=wl.hkv,
+                   dh=wl.dh, pages_per_req=pages, seed=11)
+    rng = np.random.default_rng(12)
+    pos = np.concatenate([np.arange(c, c + rows) for c in wl.ctx_lens.tolist()])
+    rej = rng.integers(0, rows, size=wl.num_reqs)
+    ds.set_step(pos, rej, np.ones(wl.num_reqs), rng.integers(0, 1000, size=wl.num_reqs),
+                rng.standard_normal((wl.num_reqs * rows, hidden * taps), dtype=np.float32))
+    ds.run()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ds.run()
+    for _ in range(3):
+        g.replay()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        g.replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    n_qkv = (wl.hq + 2 * wl.hkv) * wl.dh
+    w_bytes = 2 * (hidden * hidden * taps + 2 * wl.hkv * wl.dh * hidden + n_qkv * hidden
+                   + hidden * wl.hq * wl.dh)
+    return {"us": us, "requests": wl.num_reqs, "verified_rows_per_request": rows,
+            "block_rows_per_request": nqpr, "hidden": hidden, "taps": taps,
+            "context_rows": int(wl.total_ctx), "weight_bytes": w_bytes,
+            "stages": "prepare_inputs, fc_combine, context_kv, kv_scatter, block_qkv, "
+                      "block_attention_paged (fused q/k norm + RoPE, device-planned), o_proj",
+            "note": "one HIP graph replay per step; the weights (fc alone "
+                    f"{hidden * hidden * taps * 2 / 1e6:.0f} MB) are read once per step"}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -185,6 +233,8 @@ def main() -> int:
     ap.add_argument("--layer-hidden", type=int, default=4096,
                     help="hidden size of the draft layer whose projections around the attention "
                          "(dflash_block_qkv, dflash_o_proj) are also timed (0: skip)")
+    ap.add_argument("--draft-step-taps", type=int, default=5,
+                    help="target taps of the fc combine in the timed whole propose step (0: skip it)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
                     help="before timing, run a plain device copy of this many MiB (3 times) so a "
                          "counter profile of the same run can scale FETCH_SIZE / WRITE_SIZE")
@@ -311,6 +361,10 @@ def main() -> int:
     layer = None
     if args.layer_hidden > 0 and wl.dtype == "bf16" and not args.paged:
         layer = time_layer(wl, args.layer_hidden, stream, use_graph)
+    draft_step = None
+    if (args.draft_step_taps > 0 and args.layer_hidden > 0 and wl.dtype == "bf16"
+            and not args.paged and wl.hidden is None):
+        draft_step = time_draft_step(wl, args.layer_hidden, args.draft_step_taps, stream)
 
     cpu = None
     if args.cpu_budget > 0:
@@ -370,6 +424,7 @@ def main() -> int:
         "cpu_baseline": cpu,
         "context_kv": ckv,
         "draft_layer": layer,
+        "draft_step": draft_step,
         "algorithmic": {"attention_bytes": bytes_attn, "attention_flops": flops_attn,
                         "prologue_bytes": bytes_pro},
     }

@@ -62,7 +62,7 @@ extern "C" {
 
 const char* dflash_last_error(void) { return g_last_error.c_str(); }
 
-int dflash_abi_version(void) { return 104; }
+int dflash_abi_version(void) { return 105; }
 
 dflash_status dflash_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
                                 void* stream) {
@@ -294,9 +294,16 @@ dflash_status dflash_kv_scatter(dflash_dtype dtype, const void* k_src, const voi
                     "kv_scatter launch");
 }
 
+// Calls with fewer rows than one tile of the large-row kernel (a propose
+// step appending its verified rows) take the projection-GEMM path.
+constexpr int64_t kCtxKvRowsPath = 256;
+
 size_t dflash_context_kv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_kv_heads,
                                         int32_t head_dim) {
   if (T < 0 || hidden_size < 1 || num_kv_heads < 1 || head_dim < 1) return 0;
+  if (T < kCtxKvRowsPath)
+    return dflash::context_kv_rows_workspace_bytes(T, hidden_size, num_kv_heads, head_dim,
+                                                   kPlanComputeUnits);
   return dflash::context_kv_workspace_bytes(T, hidden_size, num_kv_heads, head_dim);
 }
 
@@ -324,7 +331,7 @@ dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, 
   const void* al[] = {hidden, hidden_norm_w, w_k, w_v, k_norm_w, rope_table, k_out, v_out};
   for (const void* t : al)
     if (!aligned(t, 16)) return fail(DFLASH_ERR_INVALID_ARG, "context_kv: tensors must be 16-byte aligned");
-  const size_t need = dflash::context_kv_workspace_bytes(T, hidden_size, num_kv_heads, head_dim);
+  const size_t need = dflash_context_kv_workspace_size(T, hidden_size, num_kv_heads, head_dim);
   if (need > 0) {
     if (!workspace) return fail(DFLASH_ERR_WORKSPACE, "context_kv: workspace is NULL (%zu bytes needed)", need);
     if (!aligned(workspace, 256))
@@ -333,6 +340,16 @@ dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, 
       return fail(DFLASH_ERR_WORKSPACE, "context_kv: workspace has %zu bytes, %zu needed",
                   workspace_bytes, need);
   }
+  if (T < kCtxKvRowsPath && hidden_size > 8192)
+    return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: calls of fewer than %lld rows need hidden_size <= 8192",
+                (long long)kCtxKvRowsPath);
+  if (T < kCtxKvRowsPath)
+    return hip_status(dflash::launch_context_kv_rows(hidden, hidden_norm_w, w_k, w_v, k_norm_w,
+                                                     positions, T, hidden_size, num_kv_heads,
+                                                     head_dim, eps, rope_table, max_pos, k_out,
+                                                     v_out, workspace, kPlanComputeUnits,
+                                                     (hipStream_t)stream),
+                      "context_kv launch");
   return hip_status(dflash::launch_context_kv(hidden, hidden_norm_w, w_k, w_v, k_norm_w, positions,
                                               T, hidden_size, num_kv_heads, head_dim, eps,
                                               rope_table, max_pos, k_out, v_out, workspace,

@@ -55,6 +55,13 @@ size_t o_proj_workspace_bytes(int64_t T, int32_t hidden, int32_t in_dim, int num
 hipError_t launch_o_proj(const void* attn, const void* w_o, int64_t T, int32_t hidden,
                          int32_t in_dim, void* out, void* ws, int num_cus, hipStream_t s);
 
+size_t context_kv_rows_workspace_bytes(int64_t T, int32_t hidden, int32_t hkv, int32_t dh,
+                                       int num_cus);
+hipError_t launch_context_kv_rows(const void* hidden, const float* hnw, const void* wk,
+                                  const void* wv, const float* knw, const int32_t* pos, int64_t T,
+                                  int32_t hidden_size, int32_t hkv, int32_t dh, float eps,
+                                  const float* table, int32_t max_pos, void* k_out, void* v_out,
+                                  void* ws, int num_cus, hipStream_t s);
 size_t fc_combine_workspace_bytes(int64_t T, int32_t hidden, int32_t taps, int num_cus);
 hipError_t launch_fc_combine(const float* aux, const void* w_fc, int64_t T, int32_t hidden,
                              int32_t taps, void* out, void* ws, int num_cus, hipStream_t s);

@@ -411,6 +411,41 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 }
 }  // namespace
 
+// Context K/V of a few rows (a propose step's appended rows): the hidden
+// RMSNorm as its own pass (bf16 rows), the K and V products on the split-K
+// projection GEMM, then the per-head k-norm + RoPE in place on K. A 256-row
+// tile of the large-row kernel would leave most CUs idle at these sizes.
+size_t context_kv_rows_workspace_bytes(int64_t T, int32_t hidden, int32_t hkv, int32_t dh,
+                                       int num_cus) {
+  return align256((size_t)T * hidden * sizeof(bf16)) +
+         align256(plan_proj(T, hkv * dh, hidden, num_cus).part_bytes);
+}
+
+hipError_t launch_context_kv_rows(const void* hidden, const float* hnw, const void* wk,
+                                  const void* wv, const float* knw, const int32_t* pos, int64_t T,
+                                  int32_t hidden_size, int32_t hkv, int32_t dh, float eps,
+                                  const float* table, int32_t max_pos, void* k_out, void* v_out,
+                                  void* ws, int num_cus, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  bf16* normed = (bf16*)ws;
+  float* part = (float*)((char*)ws + align256((size_t)T * hidden_size * sizeof(bf16)));
+  hipLaunchKernelGGL(residual_norm_kernel<false>, dim3((unsigned)T), dim3(256), 0, s,
+                     (const bf16*)hidden, (bf16*)nullptr, hnw, normed, hidden_size, eps);
+  const int32_t n = hkv * dh;
+  const ProjPlan pl = plan_proj(T, n, hidden_size, num_cus);
+  OutSegs o{};
+  o.stride[0] = o.stride[1] = o.stride[2] = n;
+  o.begin[0] = 0; o.begin[1] = o.begin[2] = o.begin[3] = n;
+  o.ptr[0] = o.ptr[1] = o.ptr[2] = (bf16*)k_out;
+  hipError_t e = launch_proj(normed, (const bf16*)wk, T, n, hidden_size, pl, part, o, s);
+  if (e != hipSuccess) return e;
+  o.ptr[0] = o.ptr[1] = o.ptr[2] = (bf16*)v_out;
+  e = launch_proj(normed, (const bf16*)wv, T, n, hidden_size, pl, part, o, s);
+  if (e != hipSuccess) return e;
+  return launch_qk_norm_rope(DFLASH_BF16, nullptr, k_out, nullptr, knw, pos, T, 0, hkv, dh, eps,
+                             table, max_pos, s);
+}
+
 size_t fc_combine_workspace_bytes(int64_t T, int32_t hidden, int32_t taps, int num_cus) {
   const int32_t k = hidden * taps;
   return align256((size_t)T * k * sizeof(bf16)) + align256(plan_proj(T, hidden, k, num_cus).part_bytes);

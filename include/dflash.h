@@ -280,9 +280,14 @@ dflash_status dflash_kv_scatter(dflash_dtype dtype, const void* k_src, const voi
  *   k_out, v_out  bf16 [T, Hkv, Dh], written
  *   workspace     device, 256-byte aligned, >= dflash_context_kv_workspace_size
  *                 bytes (no zero-fill needed)
- * Requirements: Dh == 128, H % 64 == 0, (Hkv * Dh) % 256 == 0. Each output row
- * depends only on its own input row, so splitting the rows across calls gives
- * bitwise identical results.
+ * Requirements: Dh == 128, H % 64 == 0, (Hkv * Dh) % 256 == 0. Calls of at
+ * least 256 rows fold the norm weight into the weights and run one fused
+ * GEMM + k-norm + RoPE kernel; calls of fewer rows (a propose step appending
+ * its verified rows) round the normed rows to bf16, run the split-K projection
+ * GEMM and then the k-norm + RoPE (and need H <= 8192). Each output row
+ * depends only on its own input row: splitting the rows across calls of at
+ * least 256 rows each (or of fewer than 256 rows each) gives bitwise identical
+ * results; the two forms agree within bf16 rounding.
  */
 size_t dflash_context_kv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_kv_heads,
                                         int32_t head_dim);

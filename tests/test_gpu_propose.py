@@ -262,3 +262,46 @@ def test_propose_flow_two_steps():
     fl.attend(prep0, nqpr)
     prep1 = fl.step(t_req=[nqpr] * 4, rejected=[3, 0, 7, 5], nqpr=nqpr)
     fl.attend(prep1, nqpr)
+
+
+@pytest.mark.parametrize("rows", [1, 37, 255])
+def test_context_kv_few_rows_vs_oracle(rows):
+    # calls of fewer than 256 rows (a step's appended rows) take the
+    # projection-GEMM path; scale-relative bound as for the large-row form
+    from oracle import dflash_oracle as O
+    print(f"case context_kv rows={rows}", flush=True)
+    rng = np.random.default_rng(rows)
+    h, hkv, dh = 512, 2, 128
+    hid = f32_to_bf16_bits(rng.standard_normal((rows, h), dtype=np.float32))
+    bits = lambda shape: f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02))
+    wk, wv = bits((hkv * dh, h)), bits((hkv * dh, h))
+    f = lambda n: bf16_bits_to_f32(f32_to_bf16_bits(rng.uniform(0.5, 1.5, n).astype(np.float32)))
+    hnw, knw = f(h), f(dh)
+    pos = rng.integers(0, 5000, size=rows).astype(np.int32)
+    dev = "cuda"
+    table = torch.empty((8192, dh // 2, 2), dtype=torch.float32, device=dev)
+    B.dflash_rope_table(table, 8192, dh, 1e6)
+    k = torch.empty((rows, hkv, dh), dtype=torch.bfloat16, device=dev)
+    v = torch.empty_like(k)
+    args = lambda lo, hi, ko, vo: (bits_to_device(hid[lo:hi]), torch.from_numpy(hnw).to(dev),
+                                   bits_to_device(wk), bits_to_device(wv), torch.from_numpy(knw).to(dev),
+                                   torch.from_numpy(pos[lo:hi]).to(dev), hkv, dh, 1e-6, table, ko, vo,
+                                   B.alloc_workspace(B.dflash_context_kv_workspace_size(hi - lo, h, hkv, dh)))
+    B.dflash_context_kv(*args(0, rows, k, v))
+    torch.cuda.synchronize()
+    kr, vr = O.context_kv(bf16_bits_to_f32(hid), hnw, bf16_bits_to_f32(wk), bf16_bits_to_f32(wv), knw,
+                          pos, hkv, dh, 1e-6, 1e6)
+    for name, g, o in (("K", k, kr), ("V", v, vr)):
+        rel = np.abs(to_host_f64(g) - o).max() / np.abs(o).max()
+        print(f"[context_kv rows={rows} {name}] scale-relative max err {rel:.3e}", flush=True)
+        assert rel <= 1e-2
+    if rows > 1:
+        # row independence within this form: two calls over row chunks
+        cut = rows // 3
+        for lo, hi in ((0, cut), (cut, rows)):
+            kc = torch.empty((hi - lo, hkv, dh), dtype=torch.bfloat16, device=dev)
+            vc = torch.empty_like(kc)
+            B.dflash_context_kv(*args(lo, hi, kc, vc))
+            torch.cuda.synchronize()
+            assert torch.equal(kc.view(torch.int16), k[lo:hi].view(torch.int16))
+            assert torch.equal(vc.view(torch.int16), v[lo:hi].view(torch.int16))
