@@ -12,13 +12,13 @@
 //   residual_norm_kernel  one workgroup per row: res = hidden (+ residual,
 //                         stored back as bf16), normed = bf16(res * rstd * w).
 //   proj_gemm_kernel      C[T, N] = A[T, K] * W[N, K]^T on bf16 MFMA with f32
-//                         accumulation. A workgroup owns a 128 x 64 output tile
-//                         and a slice of K; K advances 64 at a time through a
-//                         ring of LDS stages filled by direct HBM -> LDS copies
-//                         (XOR-swizzled 128-byte rows, explicit waits). With
-//                         few tiles (T ~ 128: the weights are the bytes) K is
-//                         split so that every CU streams a share of the weight;
-//                         the slices then write f32 partial tiles.
+//                         accumulation. A workgroup owns a 128 x 64 or 128 x 128
+//                         output tile and a slice of K; K advances 64 at a time
+//                         through a ring of LDS stages filled by direct HBM ->
+//                         LDS copies (XOR-swizzled 128-byte rows, explicit
+//                         waits). With few tiles (T ~ 128: the weights are the
+//                         bytes) K is split so that every CU streams a share of
+//                         the weight; the slices then write f32 partial tiles.
 //   split_sum_kernel      sums the K-slice partials and rounds to bf16.
 // Output columns go to up to three row-major destinations (q | k | v).
 #include <algorithm>
@@ -31,14 +31,24 @@ namespace dflash {
 namespace {
 
 constexpr int GBM = 128;  // output rows per workgroup tile
-constexpr int GBN = 64;   // output columns per workgroup tile
 constexpr int GBK = 64;   // K per ring stage (two MFMA k-steps of 32)
 constexpr int GNT = 256;  // threads (4 waves; wave w owns rows 32 w .. 32 w + 31)
-constexpr int GNS = 3;    // ring stages: GNS - 1 in flight
 constexpr int A_TILE = GBM * GBK;
-constexpr int W_TILE = GBN * GBK;
-constexpr int G_STAGE = A_TILE + W_TILE;  // bf16 elements per stage (24 KB)
-constexpr int LPS = (A_TILE + W_TILE) / 512 / (GNT / 64);  // wave-wide 1 KB copies per wave per stage
+// Two tile shapes: 128 x 64 with 3 stages (72 KB of LDS, two workgroups per
+// CU), and 128 x 128 with 5 stages (160 KB, one per CU) for wide outputs.
+// Each stage copies the activation slice (A) next to the weight slice (W);
+// the A slice is the same for every column tile, so a wider tile spends less
+// of the bytes a CU keeps in flight on it.
+template <int BN>
+struct GemmShape {
+  static constexpr int NS = BN == 128 ? 5 : 3;               // ring stages (NS - 1 in flight)
+  static constexpr int W_TILE = BN * GBK;
+  static constexpr int STAGE = A_TILE + W_TILE;              // bf16 elements per stage
+  static constexpr int WCP = BN / 32;                        // W copies per wave per stage
+  static constexpr int LPS = 4 + WCP;                        // copies per wave per stage
+  static constexpr int CT = BN / 16;                         // 16-column tiles per wave
+  static constexpr size_t LDS = (size_t)NS * STAGE * 2;
+};
 constexpr int NORM_MAX_CHUNKS = 4;  // 8-element chunks per thread in the row norm (H <= 8192)
 
 template <int N>
@@ -150,28 +160,32 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(const bf16* __restri
 }
 
 // ---------------------------------------------------------------------------
-// C = A * W^T over one K slice of one 128 x 64 tile.
+// C = A * W^T over one K slice of one 128 x BN tile.
 struct GemmArgs {
   const bf16* a;  // [T, K]
   const bf16* w;  // [N, K]
   int64_t T;
-  int32_t N, K, kslice, nsplit;
+  int32_t N, K;
+  int32_t ksteps;  // GBK-steps per K slice (the last slice may be shorter)
+  int32_t nsplit;
   float* part;  // [nsplit][T][N] f32 when nsplit > 1
   OutSegs out;
 };
 
+template <int BN>
 __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
+  using S = GemmShape<BN>;
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
-  const int32_t ntn = g.N / GBN;
+  const int32_t ntn = g.N / BN;
   int64_t id = blockIdx.x;
   const int32_t nt = (int32_t)(id % ntn);
   id /= ntn;
   const int32_t ks = (int32_t)(id % g.nsplit);
   const int64_t mt = id / g.nsplit;
   const int64_t m0 = mt * GBM;
-  const int32_t n0 = nt * GBN;
-  const int32_t kbeg = ks * g.kslice;
-  const int32_t nk = g.kslice / GBK;
+  const int32_t n0 = nt * BN;
+  const int32_t kbeg = ks * g.ksteps * GBK;
+  const int32_t nk = max(0, min(g.ksteps, g.K / GBK - ks * g.ksteps));
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -184,7 +198,7 @@ __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
   // Rows past T re-read row T - 1 (their results are never stored).
   const int r8 = lane >> 3, pc = lane & 7;
   int64_t a_src[4];
-  int64_t w_src[2];
+  int64_t w_src[S::WCP];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int row = (w * 4 + i) * 8 + r8;
@@ -192,53 +206,54 @@ __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
     a_src[i] = grow * g.K + swz(row, pc) * 8;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int row = (w * 2 + i) * 8 + r8;
+  for (int i = 0; i < S::WCP; ++i) {
+    const int row = (w * S::WCP + i) * 8 + r8;
     w_src[i] = (int64_t)(n0 + row) * g.K + swz(row, pc) * 8;
   }
   auto issue = [&](int32_t kt) {
     const int32_t k0 = kbeg + kt * GBK;
-    bf16* st = smem + (kt % GNS) * G_STAGE;
+    bf16* st = smem + (kt % S::NS) * S::STAGE;
 #pragma unroll
     for (int i = 0; i < 4; ++i) lds_copy16(g.a + a_src[i] + k0, st + (w * 4 + i) * 8 * GBK);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) lds_copy16(g.w + w_src[i] + k0, st + A_TILE + (w * 2 + i) * 8 * GBK);
+    for (int i = 0; i < S::WCP; ++i)
+      lds_copy16(g.w + w_src[i] + k0, st + A_TILE + (w * S::WCP + i) * 8 * GBK);
   };
 
-  f32x4 acc[2][4];
+  f32x4 acc[2][S::CT];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-    for (int ct = 0; ct < 4; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ct = 0; ct < S::CT; ++ct) acc[rt][ct] = f32x4{0.f, 0.f, 0.f, 0.f};
 
 #pragma unroll
-  for (int kt = 0; kt < GNS - 1; ++kt)
+  for (int kt = 0; kt < S::NS - 1; ++kt)
     if (kt < nk) issue(kt);
   for (int32_t kt = 0; kt < nk; ++kt) {
     // own copies of stage kt landed (later stages may stay in flight); the
     // barrier makes every wave's part visible and frees stage kt - 1
-    wait_vmcnt_steps<LPS, GNS - 2>(nk - 1 - kt);
+    wait_vmcnt_steps<S::LPS, S::NS - 2>(nk - 1 - kt);
     block_barrier();
-    if (kt + GNS - 1 < nk) issue(kt + GNS - 1);
-    const bf16* st = smem + (kt % GNS) * G_STAGE;
+    if (kt + S::NS - 1 < nk) issue(kt + S::NS - 1);
+    const bf16* st = smem + (kt % S::NS) * S::STAGE;
 #pragma unroll
     for (int ss = 0; ss < 2; ++ss) {
       const int c = 4 * ss + j;  // logical 16-byte chunk (k = 8 c .. 8 c + 7)
-      bf16x8 af[2], bf[4];
+      bf16x8 af[2], bf[S::CT];
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt) {
         const int row = 32 * w + 16 * rt + m;
         af[rt] = *reinterpret_cast<const bf16x8*>(st + row * GBK + swz(row, c) * 8);
       }
 #pragma unroll
-      for (int ct = 0; ct < 4; ++ct) {
+      for (int ct = 0; ct < S::CT; ++ct) {
         const int row = 16 * ct + m;
         bf[ct] = *reinterpret_cast<const bf16x8*>(st + A_TILE + row * GBK + swz(row, c) * 8);
       }
 #pragma unroll
       for (int rt = 0; rt < 2; ++rt)
 #pragma unroll
-        for (int ct = 0; ct < 4; ++ct)
+        for (int ct = 0; ct < S::CT; ++ct)
           acc[rt][ct] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[rt], bf[ct], acc[rt][ct], 0, 0, 0);
     }
   }
@@ -256,7 +271,7 @@ __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
         const int64_t t = m0 + 32 * w + 16 * rt + 4 * j + i;
         if (t < g.T) {
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) base[t * stride + col + 16 * ct + m] = f2bf(acc[rt][ct][i]);
+          for (int ct = 0; ct < S::CT; ++ct) base[t * stride + col + 16 * ct + m] = f2bf(acc[rt][ct][i]);
         }
       }
   } else {
@@ -268,7 +283,7 @@ __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
         const int64_t t = m0 + 32 * w + 16 * rt + 4 * j + i;
         if (t < g.T) {
 #pragma unroll
-          for (int ct = 0; ct < 4; ++ct) p[t * g.N + n0 + 16 * ct + m] = acc[rt][ct][i];
+          for (int ct = 0; ct < S::CT; ++ct) p[t * g.N + n0 + 16 * ct + m] = acc[rt][ct][i];
         }
       }
   }
@@ -301,21 +316,42 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
 
 struct ProjPlan {
   int64_t mtiles;
-  int32_t ntiles, nsplit, kslice;
+  int32_t bn, ntiles, nsplit, ksteps;
   size_t part_bytes;
 };
 
-// K is split (in powers of two, slices of at least 256) until the tiles
-// cover the CUs.
+// Wide outputs (N a multiple of 128 with at least 16 column tiles) use the
+// 128 x 128 tile, one workgroup per CU, when each workgroup then still gets a
+// long K slice (>= 12 steps): K is cut into nsplit slices of whole GBK-steps
+// (the last one may be shorter) so that the tiles make at most one round of
+// the CUs. With short slices the per-workgroup start-up and the partial tiles
+// (64 KB each) outweigh the smaller activation share (measured: o_proj of the
+// Qwen3-8B shape, 8 slices of 8 steps, 13.8 us against 10.8 us with 128 x 64
+// tiles). Otherwise 128 x 64 tiles with K split in powers of two (slices of
+// at least 256) until the tiles cover the CUs.
 ProjPlan plan_proj(int64_t T, int32_t N, int32_t K, int num_cus) {
   ProjPlan pl{};
   pl.mtiles = (T + GBM - 1) / GBM;
-  pl.ntiles = N / GBN;
-  pl.nsplit = 1;
-  const int64_t tiles = pl.mtiles * pl.ntiles;
-  while (tiles * pl.nsplit < num_cus && K % (pl.nsplit * 2 * GBK) == 0 && K / (pl.nsplit * 2) >= 256)
-    pl.nsplit *= 2;
-  pl.kslice = K / pl.nsplit;
+  const int32_t steps = K / GBK;
+  int64_t ns = 1;
+  if (N % 128 == 0 && N / 128 >= 16) {
+    const int64_t tiles = pl.mtiles * (N / 128);
+    ns = std::max<int64_t>(1, num_cus / std::max<int64_t>(1, tiles));
+  }
+  if (N % 128 == 0 && N / 128 >= 16 && steps / ns >= 12) {
+    pl.bn = 128;
+    pl.ntiles = N / 128;
+    pl.ksteps = (int32_t)((steps + ns - 1) / ns);
+    pl.nsplit = (steps + pl.ksteps - 1) / pl.ksteps;  // no empty slice
+  } else {
+    pl.bn = 64;
+    pl.ntiles = N / 64;
+    pl.nsplit = 1;
+    const int64_t tiles = pl.mtiles * pl.ntiles;
+    while (tiles * pl.nsplit < num_cus && K % (pl.nsplit * 2 * GBK) == 0 && K / (pl.nsplit * 2) >= 256)
+      pl.nsplit *= 2;
+    pl.ksteps = steps / pl.nsplit;
+  }
   pl.part_bytes = pl.nsplit > 1 ? (size_t)pl.nsplit * (size_t)T * (size_t)N * sizeof(float) : 0;
   return pl;
 }
@@ -324,22 +360,27 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 hipError_t launch_proj(const bf16* a, const bf16* w, int64_t T, int32_t N, int32_t K,
                        const ProjPlan& pl, float* part, const OutSegs& out, hipStream_t s) {
-  // 72 KB of LDS per workgroup (three stages). The limit is a per-function
-  // setting: raised once per device, not per launch (stream capture then
-  // sees only the launches).
+  // The LDS limit is a per-function setting: raised once per device, not per
+  // launch (stream capture then sees only the launches).
   static std::once_flag once[64];
   int dev = 0;
   (void)hipGetDevice(&dev);
   std::call_once(once[dev & 63], [] {
-    (void)hipFuncSetAttribute((const void*)proj_gemm_kernel, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              GNS * G_STAGE * (int)sizeof(bf16));
+    (void)hipFuncSetAttribute((const void*)proj_gemm_kernel<64>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<64>::LDS);
+    (void)hipFuncSetAttribute((const void*)proj_gemm_kernel<128>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)GemmShape<128>::LDS);
   });
   GemmArgs g{};
   g.a = a; g.w = w; g.T = T; g.N = N; g.K = K;
-  g.kslice = pl.kslice; g.nsplit = pl.nsplit; g.part = part; g.out = out;
+  g.ksteps = pl.ksteps; g.nsplit = pl.nsplit; g.part = part; g.out = out;
   const int64_t blocks = pl.mtiles * pl.ntiles * pl.nsplit;
-  hipLaunchKernelGGL(proj_gemm_kernel, dim3((unsigned)blocks), dim3(GNT),
-                     (size_t)GNS * G_STAGE * sizeof(bf16), s, g);
+  if (pl.bn == 128)
+    hipLaunchKernelGGL(proj_gemm_kernel<128>, dim3((unsigned)blocks), dim3(GNT), GemmShape<128>::LDS,
+                       s, g);
+  else
+    hipLaunchKernelGGL(proj_gemm_kernel<64>, dim3((unsigned)blocks), dim3(GNT), GemmShape<64>::LDS,
+                       s, g);
   if (pl.nsplit > 1) {
     const int64_t items = T * (N / 8);
     const int64_t sblocks = std::min<int64_t>((items + 255) / 256, 4096);

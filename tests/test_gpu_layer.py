@@ -49,6 +49,9 @@ QKV_CASES = {
              256, True),
     "unsplit_2048_rows": (dict(name="large_decode", num_reqs=128, ctx_lo=4, ctx_hi=8, hq=4, hkv=2),
                           256, True),
+    # block_qkv on 128-column tiles with uneven K slices (5 slices of 13, 13,
+    # 13, 13 and 12 steps of 64), 32 rows of a 128-row tile
+    "wide_h4096": (dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=60), 4096, True),
 }
 
 
@@ -93,7 +96,7 @@ def test_block_qkv_vs_oracle(case):
         assert np.array_equal(got, want), "residual stream != bf16(hidden + residual)"
 
 
-@pytest.mark.parametrize("case", ["two_reqs_h512", "ragged_blocks", "unsplit_2048_rows"])
+@pytest.mark.parametrize("case", ["two_reqs_h512", "ragged_blocks", "unsplit_2048_rows", "wide_h4096"])
 def test_o_proj_vs_oracle(case):
     from oracle import dflash_oracle as O
     print(f"case o_proj {case}", flush=True)

@@ -109,7 +109,7 @@ def test_prepare_inputs_random(seed):
     _assert_prep_equal(_run_prep(b), O.prepare_dflash_inputs(**b), f"seed {seed}")
 
 
-@pytest.mark.parametrize("shape", [(7, 256, 3), (128, 512, 5), (300, 128, 2)])
+@pytest.mark.parametrize("shape", [(7, 256, 3), (128, 512, 5), (300, 128, 2), (64, 2048, 6)])
 def test_fc_combine_vs_oracle(shape):
     from oracle import dflash_oracle as O
     t, h, taps = shape
