@@ -114,7 +114,16 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(const bf16* __restri
   const int tid = threadIdx.x;
   const int nch = H / 8;
   float x[NORM_MAX_CHUNKS][8];
+  float4 wr[NORM_MAX_CHUNKS][2];  // the weights, loaded with the rows (one round trip)
   float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < NORM_MAX_CHUNKS; ++i) {
+    const int c = tid + 256 * i;
+    if (c < nch) {
+      wr[i][0] = *reinterpret_cast<const float4*>(w + 8 * c);
+      wr[i][1] = *reinterpret_cast<const float4*>(w + 8 * c + 4);
+    }
+  }
 #pragma unroll
   for (int i = 0; i < NORM_MAX_CHUNKS; ++i) {
     const int c = tid + 256 * i;
@@ -148,8 +157,7 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(const bf16* __restri
   for (int i = 0; i < NORM_MAX_CHUNKS; ++i) {
     const int c = tid + 256 * i;
     if (c < nch) {
-      const float4 w0 = *reinterpret_cast<const float4*>(w + 8 * c);
-      const float4 w1 = *reinterpret_cast<const float4*>(w + 8 * c + 4);
+      const float4 w0 = wr[i][0], w1 = wr[i][1];
       const float wv[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
       bf16x8 o;
 #pragma unroll
@@ -289,7 +297,10 @@ __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
   }
 }
 
-// Sum of the K-slice partials, 8 columns a thread, in slice order.
+// Sum of the K-slice partials, 8 columns a thread, in slice order. The
+// partials of up to SB slices are loaded before any is added, so that their
+// loads are in flight together (one memory round trip per SB slices).
+constexpr int SB = 8;
 __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part,
                                                         int32_t nsplit, int64_t T, int32_t N,
                                                         OutSegs out) {
@@ -300,11 +311,22 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
     const int64_t t = i / n8;
     const int32_t n = (int32_t)(i - t * n8) * 8;
     float s[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int32_t k = 0; k < nsplit; ++k) {
-      const float4* p = reinterpret_cast<const float4*>(part + ((int64_t)k * T + t) * N + n);
-      const float4 a = p[0], b = p[1];
-      s[0] += a.x; s[1] += a.y; s[2] += a.z; s[3] += a.w;
-      s[4] += b.x; s[5] += b.y; s[6] += b.z; s[7] += b.w;
+    for (int32_t k0 = 0; k0 < nsplit; k0 += SB) {
+      float4 a[SB], b[SB];
+#pragma unroll
+      for (int kk = 0; kk < SB; ++kk) {
+        const int32_t k = min(k0 + kk, nsplit - 1);
+        const float4* p = reinterpret_cast<const float4*>(part + ((int64_t)k * T + t) * N + n);
+        a[kk] = p[0];
+        b[kk] = p[1];
+      }
+#pragma unroll
+      for (int kk = 0; kk < SB; ++kk) {
+        if (k0 + kk < nsplit) {
+          s[0] += a[kk].x; s[1] += a[kk].y; s[2] += a[kk].z; s[3] += a[kk].w;
+          s[4] += b[kk].x; s[5] += b[kk].y; s[6] += b[kk].z; s[7] += b[kk].w;
+        }
+      }
     }
     const int sg = seg_of(out, n);
     bf16x8 o;
