@@ -1213,14 +1213,19 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool p
     // merge and spread each unit's start-up over more tiles, which measured
     // faster than filling both slots. With more pairs, one round of slots,
     // then two units per pair or two rounds.
+    // Long units (over ~1536 keys at one per compute unit) fill both slots
+    // instead: measured 63.0 vs 64.2 us (16 requests x 4111 keys) and 110.3
+    // vs 113.0 us (4 x 32768 keys), while short ones (8 requests x ~1400
+    // keys) are fastest at one unit per compute unit.
     pl.chunk = 0;
     const int64_t cus = num_cus > 0 ? num_cus : 256;
     const int64_t per_cu = std::max<int64_t>(1, cus / p.num_kv_heads);
     const int64_t slots_per_head = std::max<int64_t>(1, 2 * cus / p.num_kv_heads);
     const int64_t base = (int64_t)p.num_reqs * pl.qtiles;
-    pl.units = (2 * base <= per_cu)           ? per_cu
-               : (2 * base <= slots_per_head) ? slots_per_head
-                                              : std::max(2 * base, 2 * slots_per_head);
+    const bool long_units = eff * pl.qtiles > (int64_t)1536 * per_cu;
+    pl.units = (2 * base <= per_cu && !long_units) ? per_cu
+               : (2 * base <= slots_per_head)      ? slots_per_head
+                                                   : std::max(2 * base, 2 * slots_per_head);
   }
   pl.units_pref = pl.units;
   if (paged && p.split_keys == 0) {
