@@ -203,6 +203,13 @@ def test_layer_workspace_sizes(lib):
     assert B.dflash_o_proj_workspace_size(4096, 4096, 4096) == 0
     assert B.dflash_o_proj_workspace_size(128, 4096, 4096) >= 2 * 128 * 4096 * 4
     assert B.dflash_block_qkv_workspace_size(-1, 4096, 32, 8, 128) == 0
+    # the host plan of the projections at 128 rows: q/k/v (N = 6144, K = 4096) on
+    # 48 wide column tiles x 5 uneven K slices; o_proj (8 steps a slice on wide
+    # tiles: too short) on 64 narrow tiles x 4 slices; the fc combine (K = 5 x
+    # 4096) on 32 wide tiles x 8 slices; one f32 [T, N] partial per slice
+    assert small == 128 * 4096 * 2 + 5 * 128 * 6144 * 4
+    assert B.dflash_o_proj_workspace_size(128, 4096, 4096) == 4 * 128 * 4096 * 4
+    assert B.dflash_fc_combine_workspace_size(128, 4096, 5) == 128 * 20480 * 2 + 8 * 128 * 4096 * 4
 
 
 def test_workspace_sizes(lib):
