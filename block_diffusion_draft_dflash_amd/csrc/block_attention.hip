@@ -631,8 +631,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   float2* const s_cs = reinterpret_cast<float2*>(s_op + 256);
   constexpr int CPR = DH / 4;    // 16-byte chunks per cos/sin row
   constexpr int RPD = 64 / CPR;  // cos/sin rows per wave-wide copy (1 KB)
+  // The rows sit CSTR float2 apart, 16 bytes more than a row: the lanes that
+  // read the same pair of dims of 8 different rows then hit 8 different banks
+  // (at a 512-byte stride they all hit the same one).
+  constexpr int CSTR = DH / 2 + 2;
   const int32_t ncopy = (un.blen + RPD - 1) / RPD;
-  const bool op_lds = FUSE && un.blen > 0 && 1024 * (1 + ncopy) <= STAGE_ELEMS * (int)sizeof(bf16);
+  const bool op_lds = FUSE && un.blen > 0 &&
+                      1024 + ncopy * RPD * CSTR * (int)sizeof(float2) <= STAGE_ELEMS * (int)sizeof(bf16);
   if constexpr (FUSE) {
     // The positions travel like the tiles (a direct copy into LDS, waited on
     // explicitly), ahead of them, so that reading them waits for this copy
@@ -667,12 +672,20 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
       const int32_t row = min(c * RPD + lane / CPR, un.blen - 1);
       const int32_t pos = clamp_pos(s_pos[min(row, 63)], a.max_pos);
       const float2* src = a.rope + (int64_t)pos * (DH / 2) + (lane % CPR) * 2;
-      const uint32_t lds_cs =
-          __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)(s_cs + c * RPD * (DH / 2)));
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :
-                   : "s"(lds_cs), "v"(src)
-                   : "memory", "m0");
+      // one copy per row (its CPR lanes active): a lane's 16 bytes land at
+      // M0 + 16 * lane, so M0 is the row's slot minus its first lane's offset
+#pragma unroll
+      for (int g2 = 0; g2 < RPD; ++g2) {
+        if (lane / CPR == g2) {
+          const uint32_t lds_cs =
+              __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)(s_cs + (c * RPD + g2) * CSTR)) -
+              (uint32_t)(g2 * CPR * 16);
+          asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                       :
+                       : "s"(lds_cs), "v"(src)
+                       : "memory", "m0");
+        }
+      }
     }
   }
   // Settle q, the prologue operands and the first copies once, before the
@@ -685,7 +698,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     // q: RMSNorm + RoPE in registers (rows of this lane group).
     if (op_lds) {
       load_rope_weights<DH>(s_op, j, ops);
-      load_rope_cs<DH>(s_cs + min(max(b, 0), un.blen - 1) * (DH / 2), j, ops);
+      load_rope_cs<DH>(s_cs + min(max(b, 0), un.blen - 1) * CSTR, j, ops);
     } else {
       const int32_t pos_q = rvalid ? s_pos[min(b, 63)] : 0;
       load_rope_weights<DH>(a.qnw, j, ops);
@@ -711,7 +724,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
         kx[ds] = kv ? *reinterpret_cast<const bf16x8*>(kr + swz_k<DH>(row, j + 4 * ds) * 8) : bf16x8{};
       if (op_lds) {
         load_rope_weights<DH>(s_op + DH, j, ops);
-        load_rope_cs<DH>(s_cs + min(max(kb_row, 0), un.blen - 1) * (DH / 2), j, ops);
+        load_rope_cs<DH>(s_cs + min(max(kb_row, 0), un.blen - 1) * CSTR, j, ops);
       } else {
         const int32_t pos_k = kv ? s_pos[min(kb_row, 63)] : 0;
         load_rope_weights<DH>(a.knw, j, ops);
