@@ -425,18 +425,23 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   if (a.hs.nreq > 0) {
     // planned on the host: the unit's request and its numbers are kernel arguments
     if (u >= a.hs.nunits) return;
+    // Lane l loads request l's record while the launch-order entry is
+    // fetched, and the unit's request is then read from its lane: one memory
+    // round trip for the unit's numbers instead of two dependent ones.
+    const ReqSched q = a.hs.req[min((int32_t)(threadIdx.x & 63), a.hs.nreq - 1)];
     const int32_t e = a.hs.order[u];
     const int32_t r = e >> 8;
     const int32_t loc = e & 255;
-    const ReqSched& q = a.hs.req[r];
-    u = q.ubase + loc;
+    auto pick = [&](int32_t v) { return __builtin_amdgcn_readlane(v, r); };
+    const int32_t ns = pick(q.ns), ubase = pick(q.ubase);
+    u = ubase + loc;
     un.r = r;
-    un.qt = loc / q.ns;
-    un.s = loc - un.qt * q.ns;
-    un.nsplit = q.ns;
-    un.first = q.ubase + un.qt * q.ns;
-    un.clen = q.clen; un.blen = q.blen; un.lo = q.lo; un.csz = q.csz;
-    un.ctx0 = q.c0; un.blk0 = q.b0;
+    un.qt = loc / ns;
+    un.s = loc - un.qt * ns;
+    un.nsplit = ns;
+    un.first = ubase + un.qt * ns;
+    un.clen = pick(q.clen); un.blen = pick(q.blen); un.lo = pick(q.lo); un.csz = pick(q.csz);
+    un.ctx0 = pick(q.c0); un.blk0 = pick(q.b0);
   } else {
     const ReqView rv(a);
     const int32_t chunk = __builtin_amdgcn_readfirstlane(choose_chunk(a, rv));
