@@ -80,7 +80,10 @@ struct AttnArgs {
   int32_t* dir;       // [R][qtiles][hkv]: first unit index of each split set
   int64_t total_ctx, total_blk;
   int32_t* hdr;       // workspace header: [0] = keys per split chosen for this call
-  int32_t num_reqs, hq, hkv, group, qtiles, max_blk;
+  // the merge kernel reads hkv .. hplan together (one scalar load)
+  int32_t hq, hkv, group, qtiles, num_reqs;
+  int32_t hplan;      // = hs.nreq
+  int32_t max_blk;
   int32_t chunk;      // keys per split (multiple of KT), or 0: chosen on the device
   int32_t units;      // work units per kv-head in the grid (grid = units * hkv)
   int32_t units_pref; // unit budget tried first (the packed call's; <= units)
@@ -419,12 +422,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   static_assert(LPW >= 1, "tile too small");
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][K | V][KT][DH]
 
-  const int32_t g = blockIdx.x % a.hkv;
-  int32_t u = blockIdx.x / a.hkv;  // canonical unit index (partial slot)
+  // read together before any branch (one scalar round trip)
+  const int32_t hkv = a.hkv, hnreq = a.hs.nreq, hnunits = a.hs.nunits;
+  const int32_t g = blockIdx.x % hkv;
+  int32_t u = blockIdx.x / hkv;  // canonical unit index (partial slot)
   Unit un;
-  if (a.hs.nreq > 0) {
+  const bool host_plan = hnreq > 0;
+  if (host_plan & (u >= hnunits)) return;  // (no short circuit: both loads up front)
+  if (host_plan) {
     // planned on the host: the unit's request and its numbers are kernel arguments
-    if (u >= a.hs.nunits) return;
     // Lane l loads request l's record while the launch-order entry is
     // fetched, and the unit's request is then read from its lane: one memory
     // round trip for the unit's numbers instead of two dependent ones.
@@ -903,23 +909,34 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
   constexpr int RPW = NT / TPR;           // rows per workgroup pass
   constexpr int MB = 8;
   const int32_t rb_count = QROWS / MROWS;
+  // What the host-planned path needs is read before any branch: the scalar
+  // arguments and, lane l, request l's record (zeros past the requests), so
+  // one memory round trip precedes the partials' loads.
+  const int32_t hkv = a.hkv, qtiles = a.qtiles, nreqs = a.num_reqs, hplan = a.hplan;
+  const int32_t group = a.group;
+  const ReqSched ql = a.hs.req[threadIdx.x & 63];
   int64_t id = blockIdx.x;
   const int32_t rb = (int32_t)(id % rb_count); id /= rb_count;
-  const int32_t g = (int32_t)(id % a.hkv); id /= a.hkv;
-  const int32_t qt = (int32_t)(id % a.qtiles); id /= a.qtiles;
+  const int32_t g = (int32_t)(id % hkv); id /= hkv;
+  const int32_t qt = (int32_t)(id % qtiles); id /= qtiles;
   const int32_t r = (int32_t)id;
-  if (r >= a.num_reqs) return;
+  const int32_t rl = min(r, HS_MAX_REQS - 1);
+  const int32_t h_ns = __builtin_amdgcn_readlane(ql.ns, rl);
+  const int32_t h_blen = __builtin_amdgcn_readlane(ql.blen, rl);
+  const int32_t h_b0 = __builtin_amdgcn_readlane(ql.b0, rl);
+  const int32_t h_ubase = __builtin_amdgcn_readlane(ql.ubase, rl);
+  // host plan: unsplit sets wrote their output directly
+  const bool done = (r >= nreqs) | ((hplan > 0) & ((h_ns <= 1) | (qt * QROWS >= group * h_blen)));
+  if (done) return;
   int32_t ns, blen, b0, first;
-  if (a.hs.nreq > 0) {
-    const ReqSched& q = a.hs.req[r];
-    ns = q.ns; blen = q.blen; b0 = q.b0;
-    if (ns <= 1 || qt * QROWS >= a.group * blen) return;
-    first = q.ubase + qt * ns;
+  if (hplan > 0) {
+    ns = h_ns; blen = h_blen; b0 = h_b0;
+    first = h_ubase + qt * ns;
   } else {
     // The split size (chosen by the main kernel of this call unless fixed), the
     // directory entry and the lengths are independent loads.
     const int32_t chunk = a.chunk > 0 ? a.chunk : a.hdr[0];
-    first = a.dir[((int64_t)r * a.qtiles + qt) * a.hkv + g];
+    first = a.dir[((int64_t)r * qtiles + qt) * hkv + g];
     const LaneReq q = lane_req(a, r);
     if (chunk < KT) return;
     ns = req_splits(q, chunk); blen = q.blen; b0 = q.b0;
@@ -1320,6 +1337,7 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.scale_log2 = p.scale * LOG2E;
   a.causal = p.causal ? 1 : 0; a.window = p.window;
   plan_host_schedule(p, plan, pg != nullptr, &a.hs);
+  a.hplan = a.hs.nreq;
   // Host-planned: launch only the units the plan uses.
   const int64_t blocks = (a.hs.nreq > 0 ? a.hs.nunits : plan.units) * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
