@@ -229,6 +229,23 @@ def test_parity_fused_prologue(case):
     run_and_check(wl, tag=f"fused {case}", fused=True)
 
 
+@pytest.mark.parametrize("host_lengths", [True, False])
+def test_parity_fused_positions_not_after_context(host_lengths):
+    # Block rows whose positions are not C..C+B-1 (shifted per request, one
+    # request reversed): the fused prologue fetches the cos/sin rows of the
+    # positions the kernel expects first, then again for the true ones.
+    print(f"case fused shifted positions host_lengths={host_lengths}", flush=True)
+    wl = make_workload("qwen3_8b_draft", num_reqs=4, ctx_lo=60, ctx_hi=400)
+    pos = wl.blk_positions.copy()
+    for r in range(wl.num_reqs):
+        b0, b1 = int(wl.cu_blk[r]), int(wl.cu_blk[r + 1])
+        pos[b0:b1] = pos[b0:b1] + 37 * r
+        if r == 2:
+            pos[b0:b1] = pos[b0:b1][::-1]
+    wl.blk_positions = pos.astype(np.int32)
+    run_and_check(wl, tag="fused shifted positions", fused=True, host_lengths=host_lengths)
+
+
 @pytest.mark.parametrize("split", [64, 128])
 def test_parity_fused_forced_splits(split):
     # splits that cut through the block rows
