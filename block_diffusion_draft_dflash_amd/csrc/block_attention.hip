@@ -423,35 +423,44 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][K | V][KT][DH]
 
   // read together before any branch (one scalar round trip)
-  const int32_t hkv = a.hkv, hnreq = a.hs.nreq, hnunits = a.hs.nunits;
-  const int32_t g = blockIdx.x % hkv;
-  int32_t u = blockIdx.x / hkv;  // canonical unit index (partial slot)
-  Unit un;
+  // Launched as (kv-head, unit) = (blockIdx.x, blockIdx.y + 65535 blockIdx.z):
+  // the unit index needs no argument read. With the host plan, the launch-order
+  // entry (a scalar load) and, lane l, request l's record are read together
+  // with the plan's counts, all before any branch, and the unit's request is
+  // then read from its lane: the unit's numbers arrive after one memory round
+  // trip.
+  const int32_t g = blockIdx.x;
+  int32_t u = (int32_t)blockIdx.y + 65535 * (int32_t)blockIdx.z;  // canonical unit index
+  const int32_t hnreq = a.hs.nreq, hnunits = a.hs.nunits;
+  const int32_t e = a.hs.order[min(u, HS_MAX_UNITS - 1)];
+  const ReqSched q = a.hs.req[threadIdx.x & 63];
+  const int32_t hr = e >> 8;
+  // every field read from the unit's lane before any branch, so that the
+  // loads above are all issued ahead of one wait
+  auto pick = [&](int32_t v) { return __builtin_amdgcn_readlane(v, hr & (HS_MAX_REQS - 1)); };
+  const int32_t h_ns = pick(q.ns), h_ubase = pick(q.ubase), h_clen = pick(q.clen);
+  const int32_t h_blen = pick(q.blen), h_lo = pick(q.lo), h_csz = pick(q.csz);
+  const int32_t h_c0 = pick(q.c0), h_b0 = pick(q.b0);
   const bool host_plan = hnreq > 0;
-  if (host_plan & (u >= hnunits)) return;  // (no short circuit: both loads up front)
+  // (no short circuit, so that every load above stays ahead of the branch)
+  if (host_plan & ((u >= hnunits) | (hr >= HS_MAX_REQS))) return;
+  Unit un;
   if (host_plan) {
     // planned on the host: the unit's request and its numbers are kernel arguments
-    // Lane l loads request l's record while the launch-order entry is
-    // fetched, and the unit's request is then read from its lane: one memory
-    // round trip for the unit's numbers instead of two dependent ones.
-    const ReqSched q = a.hs.req[min((int32_t)(threadIdx.x & 63), a.hs.nreq - 1)];
-    const int32_t e = a.hs.order[u];
-    const int32_t r = e >> 8;
     const int32_t loc = e & 255;
-    auto pick = [&](int32_t v) { return __builtin_amdgcn_readlane(v, r); };
-    const int32_t ns = pick(q.ns), ubase = pick(q.ubase);
+    const int32_t ns = h_ns, ubase = h_ubase;
     u = ubase + loc;
-    un.r = r;
+    un.r = hr;
     un.qt = loc / ns;
     un.s = loc - un.qt * ns;
     un.nsplit = ns;
     un.first = ubase + un.qt * ns;
-    un.clen = pick(q.clen); un.blen = pick(q.blen); un.lo = pick(q.lo); un.csz = pick(q.csz);
-    un.ctx0 = pick(q.c0); un.blk0 = pick(q.b0);
+    un.clen = h_clen; un.blen = h_blen; un.lo = h_lo; un.csz = h_csz;
+    un.ctx0 = h_c0; un.blk0 = h_b0;
   } else {
     const ReqView rv(a);
     const int32_t chunk = __builtin_amdgcn_readfirstlane(choose_chunk(a, rv));
-    if (blockIdx.x == 0 && threadIdx.x == 0) a.hdr[0] = chunk;  // for the merge kernel
+    if (g == 0 && u == 0 && threadIdx.x == 0) a.hdr[0] = chunk;  // for the merge kernel
     if (!find_unit(a, rv, chunk, u, &un)) return;  // uniform over the workgroup
   }
   // Every lane holds the same unit; say so to the compiler (scalar registers,
@@ -1358,7 +1367,10 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
                               hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + (PG_MAX + POS_LDS) * 4);
   });
   const int64_t mblocks = (int64_t)p.num_reqs * plan.qtiles * p.num_kv_heads * (QROWS / MROWS);
-  const dim3 grid((unsigned)blocks), blk(NT), mgrid((unsigned)mblocks);
+  const int64_t launch_units = blocks / p.num_kv_heads;
+  const dim3 grid((unsigned)p.num_kv_heads, (unsigned)std::min<int64_t>(launch_units, 65535),
+                  (unsigned)((launch_units + 65534) / 65535));
+  const dim3 blk(NT), mgrid((unsigned)mblocks);
   if (p.head_dim == 128) {
     if (pro) hipLaunchKernelGGL((block_attn_bf16_kernel<128, true>), grid, blk, lds, s, a);
     else hipLaunchKernelGGL((block_attn_bf16_kernel<128, false>), grid, blk, lds, s, a);
