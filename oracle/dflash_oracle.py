@@ -33,7 +33,7 @@ Sources (pages of the vllm.cpp project):
     residual add + RMSNorm, the merged qkv weight applied as one product and
     split into q | k | v, and o_proj applied to the attention output.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
   * GQA: q-head h reads kv-head h // (Hq/Hkv).
   * NeoX RoPE pairs element i with element i + Dh/2; inverse frequency
     theta**(-2i/Dh); the whole head dimension rotates.
@@ -47,8 +47,8 @@ Readings taken where the pages are silent (each also listed in the design doc):
 Parity pins: every function here is pinned by ``tests/test_oracle_pins.py``
 against closed forms, invariants, library routines and brute force. No
 function is "parity unpinned" at the level of its definition; the pairing
-convention of RoPE is fixed only by the name "NeoX" on the pages (see
-DESIGN.md).
+convention of RoPE is fixed only by the name "NeoX" on the pages (both
+pairings satisfy the invariants the pins check).
 """
 from __future__ import annotations
 
