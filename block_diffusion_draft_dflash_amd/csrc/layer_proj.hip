@@ -170,8 +170,10 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(const bf16* __restri
 // ---------------------------------------------------------------------------
 // C = A * W^T over one K slice of one 128 x BN tile.
 struct GemmArgs {
-  const bf16* a;  // [T, K]
-  const bf16* w;  // [N, K]
+  const bf16* a;   // [T, K]
+  const bf16* w;   // rows [0, n1) of W: [n1, K]
+  const bf16* w2;  // rows [n1, N) of W: [N - n1, K] (n1 a multiple of the tile width)
+  int32_t n1;
   int64_t T;
   int32_t N, K;
   int32_t ksteps;  // GBK-steps per K slice (the last slice may be shorter)
@@ -213,10 +215,14 @@ __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
     const int64_t grow = min(m0 + row, g.T - 1);
     a_src[i] = grow * g.K + swz(row, pc) * 8;
   }
+  // the tile's weight rows come from one of the two sources
+  const bool second = n0 >= g.n1;
+  const bf16* const wsrc = second ? g.w2 : g.w;
+  const int32_t wn0 = second ? n0 - g.n1 : n0;
 #pragma unroll
   for (int i = 0; i < S::WCP; ++i) {
     const int row = (w * S::WCP + i) * 8 + r8;
-    w_src[i] = (int64_t)(n0 + row) * g.K + swz(row, pc) * 8;
+    w_src[i] = (int64_t)(wn0 + row) * g.K + swz(row, pc) * 8;
   }
   auto issue = [&](int32_t kt) {
     const int32_t k0 = kbeg + kt * GBK;
@@ -225,7 +231,7 @@ __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i) lds_copy16(g.a + a_src[i] + k0, st + (w * 4 + i) * 8 * GBK);
 #pragma unroll
     for (int i = 0; i < S::WCP; ++i)
-      lds_copy16(g.w + w_src[i] + k0, st + A_TILE + (w * S::WCP + i) * 8 * GBK);
+      lds_copy16(wsrc + w_src[i] + k0, st + A_TILE + (w * S::WCP + i) * 8 * GBK);
   };
 
   f32x4 acc[2][S::CT];
@@ -351,16 +357,16 @@ struct ProjPlan {
 // Qwen3-8B shape, 8 slices of 8 steps, 13.8 us against 10.8 us with 128 x 64
 // tiles). Otherwise 128 x 64 tiles with K split in powers of two (slices of
 // at least 256) until the tiles cover the CUs.
-ProjPlan plan_proj(int64_t T, int32_t N, int32_t K, int num_cus) {
+ProjPlan plan_proj(int64_t T, int32_t N, int32_t K, int num_cus, bool allow_wide = true) {
   ProjPlan pl{};
   pl.mtiles = (T + GBM - 1) / GBM;
   const int32_t steps = K / GBK;
   int64_t ns = 1;
-  if (N % 128 == 0 && N / 128 >= 16) {
+  if (allow_wide && N % 128 == 0 && N / 128 >= 16) {
     const int64_t tiles = pl.mtiles * (N / 128);
     ns = std::max<int64_t>(1, num_cus / std::max<int64_t>(1, tiles));
   }
-  if (N % 128 == 0 && N / 128 >= 16 && steps / ns >= 12) {
+  if (allow_wide && N % 128 == 0 && N / 128 >= 16 && steps / ns >= 12) {
     pl.bn = 128;
     pl.ntiles = N / 128;
     pl.ksteps = (int32_t)((steps + ns - 1) / ns);
@@ -380,8 +386,11 @@ ProjPlan plan_proj(int64_t T, int32_t N, int32_t K, int num_cus) {
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// W's rows [0, n1) are read from w and rows [n1, N) from w2 (w2 == nullptr: all
+// from w); n1 must be a multiple of the tile width.
 hipError_t launch_proj(const bf16* a, const bf16* w, int64_t T, int32_t N, int32_t K,
-                       const ProjPlan& pl, float* part, const OutSegs& out, hipStream_t s) {
+                       const ProjPlan& pl, float* part, const OutSegs& out, hipStream_t s,
+                       const bf16* w2 = nullptr, int32_t n1 = 0) {
   // The LDS limit is a per-function setting: raised once per device, not per
   // launch (stream capture then sees only the launches).
   static std::once_flag once[64];
@@ -395,6 +404,8 @@ hipError_t launch_proj(const bf16* a, const bf16* w, int64_t T, int32_t N, int32
   });
   GemmArgs g{};
   g.a = a; g.w = w; g.T = T; g.N = N; g.K = K;
+  g.w2 = w2 ? w2 : w;
+  g.n1 = w2 ? n1 : N;
   g.ksteps = pl.ksteps; g.nsplit = pl.nsplit; g.part = part; g.out = out;
   const int64_t blocks = pl.mtiles * pl.ntiles * pl.nsplit;
   if (pl.bn == 128)
@@ -475,13 +486,14 @@ __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict_
 }  // namespace
 
 // Context K/V of a few rows (a propose step's appended rows): the hidden
-// RMSNorm as its own pass (bf16 rows), the K and V products on the split-K
-// projection GEMM, then the per-head k-norm + RoPE in place on K. A 256-row
+// RMSNorm as its own pass (bf16 rows), the K and V products as one split-K
+// projection GEMM over the stacked weights, then the per-head k-norm + RoPE in
+// place on K. A 256-row
 // tile of the large-row kernel would leave most CUs idle at these sizes.
 size_t context_kv_rows_workspace_bytes(int64_t T, int32_t hidden, int32_t hkv, int32_t dh,
                                        int num_cus) {
   return align256((size_t)T * hidden * sizeof(bf16)) +
-         align256(plan_proj(T, hkv * dh, hidden, num_cus).part_bytes);
+         align256(plan_proj(T, 2 * hkv * dh, hidden, num_cus, (hkv * dh) % 128 == 0).part_bytes);
 }
 
 hipError_t launch_context_kv_rows(const void* hidden, const float* hnw, const void* wk,
@@ -494,16 +506,17 @@ hipError_t launch_context_kv_rows(const void* hidden, const float* hnw, const vo
   float* part = (float*)((char*)ws + align256((size_t)T * hidden_size * sizeof(bf16)));
   hipLaunchKernelGGL(residual_norm_kernel<false>, dim3((unsigned)T), dim3(256), 0, s,
                      (const bf16*)hidden, (bf16*)nullptr, hnw, normed, hidden_size, eps);
+  // K and V in one product over the stacked [W_k; W_v] (columns [0, Hkv Dh) to
+  // k_out, the rest to v_out)
   const int32_t n = hkv * dh;
-  const ProjPlan pl = plan_proj(T, n, hidden_size, num_cus);
+  // (a 128-wide tile must not straddle the two weights)
+  const ProjPlan pl = plan_proj(T, 2 * n, hidden_size, num_cus, n % 128 == 0);
   OutSegs o{};
+  o.ptr[0] = (bf16*)k_out; o.ptr[1] = o.ptr[2] = (bf16*)v_out;
   o.stride[0] = o.stride[1] = o.stride[2] = n;
-  o.begin[0] = 0; o.begin[1] = o.begin[2] = o.begin[3] = n;
-  o.ptr[0] = o.ptr[1] = o.ptr[2] = (bf16*)k_out;
-  hipError_t e = launch_proj(normed, (const bf16*)wk, T, n, hidden_size, pl, part, o, s);
-  if (e != hipSuccess) return e;
-  o.ptr[0] = o.ptr[1] = o.ptr[2] = (bf16*)v_out;
-  e = launch_proj(normed, (const bf16*)wv, T, n, hidden_size, pl, part, o, s);
+  o.begin[0] = 0; o.begin[1] = n; o.begin[2] = o.begin[3] = 2 * n;
+  hipError_t e = launch_proj(normed, (const bf16*)wk, T, 2 * n, hidden_size, pl, part, o, s,
+                             (const bf16*)wv, n);
   if (e != hipSuccess) return e;
   return launch_qk_norm_rope(DFLASH_BF16, nullptr, k_out, nullptr, knw, pos, T, 0, hkv, dh, eps,
                              table, max_pos, s);

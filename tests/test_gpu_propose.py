@@ -264,14 +264,17 @@ def test_propose_flow_two_steps():
     fl.attend(prep1, nqpr)
 
 
-@pytest.mark.parametrize("rows", [1, 37, 255])
-def test_context_kv_few_rows_vs_oracle(rows):
+# (the last case: 128-wide tiles, K's and V's weights as the two halves of N)
+@pytest.mark.parametrize("rows,hkv,h", [(1, 2, 512), (37, 2, 512), (255, 2, 512), (37, 4, 512),
+                                        (37, 16, 8192)])
+def test_context_kv_few_rows_vs_oracle(rows, hkv, h):
     # calls of fewer than 256 rows (a step's appended rows) take the
-    # projection-GEMM path; scale-relative bound as for the large-row form
+    # projection-GEMM path (K and V in one product over the two weights);
+    # scale-relative bound as for the large-row form
     from oracle import dflash_oracle as O
-    print(f"case context_kv rows={rows}", flush=True)
+    print(f"case context_kv rows={rows} hkv={hkv} h={h}", flush=True)
     rng = np.random.default_rng(rows)
-    h, hkv, dh = 512, 2, 128
+    dh = 128
     hid = f32_to_bf16_bits(rng.standard_normal((rows, h), dtype=np.float32))
     bits = lambda shape: f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(0.02))
     wk, wv = bits((hkv * dh, h)), bits((hkv * dh, h))
