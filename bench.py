@@ -101,6 +101,28 @@ def cpu_baseline(wl, budget_s: float):
     return el / reps, reps, threads
 
 
+def device_copy_gbs(stream, mib=512, reps=5):
+    """What a plain device-to-device copy achieves on this GPU (bytes read +
+    written per second), measured in the same run: the attainable stream rate
+    beside the nominal 8 TB/s."""
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return 2.0 * n / t / 1e9
+
+
 def time_layer(wl, hidden, stream, use_graph, reps=60):
     """The draft layer around the attention on this batch's block rows:
     dflash_block_qkv (input norm + merged q/k/v), the fused attention, and
@@ -329,6 +351,7 @@ def main() -> int:
                                             if use_graph else n_attn)
 
     bytes_attn, flops_attn, bytes_pro = algorithmic_cost(wl)
+    copy_gbs = device_copy_gbs(stream)
     step_s = ms_per_step * 1e-3
     value = flops_attn / step_s / 1e12
     tokens_per_s = wl.total_blk / step_s
@@ -420,6 +443,8 @@ def main() -> int:
             "traffic": traffic,
             "algorithmic_bytes_per_launch": bytes_attn,
             "avg_launch_us": attn_us,
+            "achievable_copy_gbs": copy_gbs,
+            "frac_of_copy": achieved_gbs / copy_gbs,
         },
         "cpu_baseline": cpu,
         "context_kv": ckv,
