@@ -351,7 +351,8 @@ def main() -> int:
                                             if use_graph else n_attn)
 
     bytes_attn, flops_attn, bytes_pro = algorithmic_cost(wl)
-    copy_gbs = device_copy_gbs(stream)
+    # (skipped in a counter-calibration run, whose copy must be the only one)
+    copy_gbs = device_copy_gbs(stream) if args.copy_calibration_mb == 0 else None
     step_s = ms_per_step * 1e-3
     value = flops_attn / step_s / 1e12
     tokens_per_s = wl.total_blk / step_s
@@ -444,7 +445,7 @@ def main() -> int:
             "algorithmic_bytes_per_launch": bytes_attn,
             "avg_launch_us": attn_us,
             "achievable_copy_gbs": copy_gbs,
-            "frac_of_copy": achieved_gbs / copy_gbs,
+            "frac_of_copy": achieved_gbs / copy_gbs if copy_gbs else None,
         },
         "cpu_baseline": cpu,
         "context_kv": ckv,
