@@ -142,6 +142,17 @@ def test_parity_forced_splits(split):
     run_and_check(wl, split_keys=split, check_intermediates=False, tag=f"split {split}")
 
 
+def test_parity_more_units_than_the_host_table():
+    # 64-key splits of ~4500-key requests: ~70 units per request, over 512 per
+    # kv-head in all, more than the host-planned table holds: the kernels plan
+    # from the device lengths instead (same bars)
+    print("case units beyond the host table", flush=True)
+    wl = make_workload("qwen3_8b_draft", num_reqs=8, ctx_lo=4000, ctx_hi=5000)
+    run_and_check(wl, split_keys=64, reqs=[0, 3, 7], check_intermediates=False,
+                  tag="units beyond the host table")
+    run_and_check(wl, split_keys=64, reqs=[1, 6], fused=True, tag="units beyond the host table, fused")
+
+
 EDGE = {
     "empty_ctx_and_blocks": dict(name="qwen3_8b_draft", ctx_lens=[0, 5, 130, 0, 77],
                                  blk_lens=[3, 0, 17, 40, 1]),
