@@ -441,6 +441,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   const int32_t h_ns = pick(q.ns), h_ubase = pick(q.ubase), h_clen = pick(q.clen);
   const int32_t h_blen = pick(q.blen), h_lo = pick(q.lo), h_csz = pick(q.csz);
   const int32_t h_c0 = pick(q.c0), h_b0 = pick(q.b0);
+  // The arguments the prologue and the first copies need, read here with the
+  // lookup (one batch of scalar loads and one wait) rather than each at its
+  // first use behind a branch (a dependent argument read each).
+  asm volatile("" ::"s"(a.q), "s"(a.kb), "s"(a.vb), "s"(a.kc), "s"(a.vc), "s"(a.bt), "s"(a.bpos),
+               "s"(a.rope), "s"(a.qnw), "s"(a.knw), "s"(a.total_blk), "s"(a.hq), "s"(a.hkv),
+               "s"(a.group), "s"(a.max_blk), "s"(a.max_pos), "s"(a.eps), "s"(a.causal),
+               "s"(a.window), "s"(a.scale_log2), "s"(a.bt_stride), "s"(a.num_pages_m1));
   const bool host_plan = hnreq > 0;
   // (no short circuit, so that every load above stays ahead of the branch)
   if (host_plan & ((u >= hnunits) | (hr >= HS_MAX_REQS))) return;
@@ -934,6 +941,8 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
   const int32_t h_blen = __builtin_amdgcn_readlane(ql.blen, rl);
   const int32_t h_b0 = __builtin_amdgcn_readlane(ql.b0, rl);
   const int32_t h_ubase = __builtin_amdgcn_readlane(ql.ubase, rl);
+  // (the pointers and sizes of the merge itself, read in the same batch)
+  asm volatile("" ::"s"(a.part_o), "s"(a.part_ml), "s"(a.out), "s"(a.total_blk), "s"(a.hq));
   // host plan: unsplit sets wrote their output directly
   const bool done = (r >= nreqs) | ((hplan > 0) & ((h_ns <= 1) | (qt * QROWS >= group * h_blen)));
   if (done) return;
