@@ -942,7 +942,8 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
   const int32_t h_b0 = __builtin_amdgcn_readlane(ql.b0, rl);
   const int32_t h_ubase = __builtin_amdgcn_readlane(ql.ubase, rl);
   // (the pointers and sizes of the merge itself, read in the same batch)
-  asm volatile("" ::"s"(a.part_o), "s"(a.part_ml), "s"(a.out), "s"(a.total_blk), "s"(a.hq));
+  asm volatile("" ::"s"(a.part_o), "s"(a.part_ml), "s"(a.out), "s"(a.total_blk), "s"(a.hq),
+               "s"(a.num_reqs), "s"(a.hplan), "s"(a.qtiles), "s"(a.hkv), "s"(a.group));
   // host plan: unsplit sets wrote their output directly
   const bool done = (r >= nreqs) | ((hplan > 0) & ((h_ns <= 1) | (qt * QROWS >= group * h_blen)));
   if (done) return;

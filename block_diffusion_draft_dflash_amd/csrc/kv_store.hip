@@ -16,6 +16,9 @@ __global__ __launch_bounds__(256) void kv_scatter_kernel(const uint4* __restrict
                                                          int64_t rows, int64_t chunks_per_row,
                                                          uint4* __restrict__ kp,
                                                          uint4* __restrict__ vp, int64_t num_slots) {
+  // every argument in one batch of scalar loads (no dependent argument reads)
+  asm volatile("" ::"s"(ks), "s"(vs), "s"(slots), "s"(rows), "s"(chunks_per_row), "s"(kp), "s"(vp),
+               "s"(num_slots));
   const int64_t total = rows * chunks_per_row;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
        i += (int64_t)gridDim.x * blockDim.x) {

@@ -109,6 +109,8 @@ __global__ __launch_bounds__(256) void residual_norm_kernel(const bf16* __restri
                                                             const float* __restrict__ w,
                                                             bf16* __restrict__ normed, int32_t H,
                                                             float eps) {
+  // every argument in one batch of scalar loads (no dependent argument reads)
+  asm volatile("" ::"s"(hidden), "s"(residual), "s"(w), "s"(normed), "s"(H), "s"(eps));
   __shared__ float red[4];
   const int64_t t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -185,6 +187,9 @@ struct GemmArgs {
 template <int BN>
 __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
   using S = GemmShape<BN>;
+  // the loader's arguments in one batch of scalar loads
+  asm volatile("" ::"s"(g.a), "s"(g.w), "s"(g.w2), "s"(g.n1), "s"(g.T), "s"(g.N), "s"(g.K),
+               "s"(g.ksteps), "s"(g.nsplit));
   extern __shared__ __attribute__((aligned(16))) bf16 smem[];
   const int32_t ntn = g.N / BN;
   int64_t id = blockIdx.x;
@@ -310,6 +315,10 @@ constexpr int SB = 8;
 __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict__ part,
                                                         int32_t nsplit, int64_t T, int32_t N,
                                                         OutSegs out) {
+  // every argument in one batch of scalar loads (no dependent argument reads)
+  asm volatile("" ::"s"(part), "s"(nsplit), "s"(T), "s"(N), "s"(out.ptr[0]), "s"(out.ptr[1]),
+               "s"(out.ptr[2]), "s"(out.stride[0]), "s"(out.stride[1]), "s"(out.stride[2]),
+               "s"(out.begin[1]), "s"(out.begin[2]));
   const int64_t n8 = N / 8;
   const int64_t total = T * n8;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
@@ -473,6 +482,7 @@ namespace {
 // f32 -> bf16 (round to nearest even), 8 elements a thread.
 __global__ __launch_bounds__(256) void cast_bf16_kernel(const float* __restrict__ src,
                                                         bf16* __restrict__ dst, int64_t n8) {
+  asm volatile("" ::"s"(src), "s"(dst), "s"(n8));  // one batch of argument loads
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n8;
        i += (int64_t)gridDim.x * blockDim.x) {
     const float4 a = reinterpret_cast<const float4*>(src)[2 * i];

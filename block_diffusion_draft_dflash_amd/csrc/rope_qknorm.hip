@@ -62,6 +62,9 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     const float* __restrict__ wk, const int32_t* __restrict__ pos,
     const float2* __restrict__ table, int32_t max_pos, int64_t rows, int32_t hq, int32_t hkv,
     float eps) {
+  // every argument in one batch of scalar loads (no dependent argument reads)
+  asm volatile("" ::"s"(q), "s"(k), "s"(wq), "s"(wk), "s"(pos), "s"(table), "s"(max_pos), "s"(rows),
+               "s"(hq), "s"(hkv), "s"(eps));
   constexpr int LANES = DH / 8;
   constexpr int PER_WAVE = 64 / LANES;
   constexpr int HALF = DH / 2;
