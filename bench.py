@@ -357,7 +357,10 @@ def main() -> int:
     value = flops_attn / step_s / 1e12
     tokens_per_s = wl.total_blk / step_s
     achieved_gbs = bytes_attn / (attn_us * 1e-6) / 1e9
-    traffic = committed_traffic(args.workload)
+    # the counters were taken on the default launch (packed store, fused
+    # prologue, host-planned split): another launch gets no traffic figure
+    default_launch = not (args.paged or args.unfused or args.device_plan or args.split_keys)
+    traffic = committed_traffic(args.workload) if default_launch else None
 
     # Context-K/V precompute (hidden-state workloads): the dflash_context_kv
     # call (weight fold, row rms, fused GEMM + k-norm + RoPE), HIP events on
