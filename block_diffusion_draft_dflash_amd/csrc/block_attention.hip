@@ -561,11 +561,13 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   // insertion cannot tell which LDS stage a later LDS read touches and would
   // otherwise drain every copy in flight before it. All waits on these copies
   // are explicit (wait_vmcnt below); no other vector-memory load is in flight
-  // while they are.
+  // while they are. Each K/V byte is read once per call, so the copies carry
+  // the non-temporal hint (measured 3-11% faster per call than the default
+  // policy).
   auto dma = [](const bf16* src, bf16* dst) {
     const uint32_t lds_addr =
         __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)dst);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
                  :
                  : "s"(lds_addr), "v"(src)
                  : "memory", "m0");

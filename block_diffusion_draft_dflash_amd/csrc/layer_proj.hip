@@ -88,6 +88,16 @@ __device__ __forceinline__ void lds_copy16(const void* src, void* dst) {
                : "s"(lds), "v"(src)
                : "memory", "m0");
 }
+// The same copy with the non-temporal hint, for data read once per call (the
+// weight slices): it streams through the caches instead of displacing the
+// activations that every column tile re-reads.
+__device__ __forceinline__ void lds_copy16_nt(const void* src, void* dst) {
+  const uint32_t lds = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)dst);
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off nt"
+               :
+               : "s"(lds), "v"(src)
+               : "memory", "m0");
+}
 // Physical 16-byte chunk of logical chunk c in a 128-byte LDS row.
 __device__ __forceinline__ int swz(int row, int c) { return c ^ (row & 7); }
 
@@ -236,7 +246,7 @@ __global__ __launch_bounds__(GNT) void proj_gemm_kernel(GemmArgs g) {
     for (int i = 0; i < 4; ++i) lds_copy16(g.a + a_src[i] + k0, st + (w * 4 + i) * 8 * GBK);
 #pragma unroll
     for (int i = 0; i < S::WCP; ++i)
-      lds_copy16(wsrc + w_src[i] + k0, st + A_TILE + (w * S::WCP + i) * 8 * GBK);
+      lds_copy16_nt(wsrc + w_src[i] + k0, st + A_TILE + (w * S::WCP + i) * 8 * GBK);
   };
 
   f32x4 acc[2][S::CT];
