@@ -226,6 +226,11 @@ FUSED = {
     "empty_ctx_and_blocks": dict(name="qwen3_8b_draft", ctx_lens=[0, 5, 130, 0, 77],
                                  blk_lens=[3, 0, 17, 40, 1]),
     "block_64": dict(name="swa", ctx_lens=[40, 301], blk_lens=[64, 33], window=50),
+    # bidirectional blocks that start at the last key of a 32-key tile: 64
+    # (and 34) block rows then span three tiles, all normalised in LDS before
+    # the loop
+    "block_64_three_tiles": dict(name="qwen3_8b_draft", ctx_lens=[31, 95, 63, 0],
+                                 blk_lens=[64, 64, 34, 64]),
     "dh64": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=50, ctx_hi=300, hq=8, hkv=2, dh=64),
     "gqa8": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=200, hq=64, hkv=8),
 }
