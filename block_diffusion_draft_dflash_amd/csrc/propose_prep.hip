@@ -44,16 +44,35 @@ __global__ __launch_bounds__(PT) void prepare_inputs_kernel(dflash_prepare_param
   const int32_t nqpr = p.num_query_per_req, nspec = p.num_speculative_steps;
   const int32_t R = p.num_reqs;
   if (r == R) {
-    if (tid == 0) {
-      // running sum over the requests, in order (one thread: R is small)
-      int32_t acc = 0;
-      out.ctx_cu[0] = 0;
-      for (int32_t i = 0; i < R; ++i) {
-        acc += (int32_t)(last_kept_pos(p, in, i) + 1);
-        out.ctx_cu[i + 1] = acc;
+    // Running sum of the kept-context lengths over the requests, PT requests
+    // at a time: every thread loads its request's length (the loads of a
+    // chunk are in flight together), then an inclusive scan across the
+    // workgroup plus the carry of the chunks before. Unsigned arithmetic: the
+    // same bits as the in-order two's-complement sum.
+    __shared__ uint32_t wsum[PT / 64];
+    uint32_t carry = 0;
+    if (tid == 0) out.ctx_cu[0] = 0;
+    for (int32_t base = 0; base < R; base += PT) {
+      const int32_t i = base + tid;
+      uint32_t x = i < R ? (uint32_t)(int32_t)(last_kept_pos(p, in, i) + 1) : 0u;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t y = __shfl_up(x, d, 64);
+        if ((tid & 63) >= d) x += y;
       }
-      for (int32_t i = R + 1; i <= p.max_num_reqs; ++i) out.ctx_cu[i] = acc;
+      if ((tid & 63) == 63) wsum[tid >> 6] = x;
+      __syncthreads();
+      uint32_t before = carry, total = 0;
+#pragma unroll
+      for (int wv = 0; wv < PT / 64; ++wv) {
+        before += wv < (tid >> 6) ? wsum[wv] : 0u;
+        total += wsum[wv];
+      }
+      if (i < R) out.ctx_cu[i + 1] = (int32_t)(before + x);
+      carry += total;
+      __syncthreads();  // wsum is rewritten by the next chunk
     }
+    for (int64_t i = (int64_t)R + 1 + tid; i <= p.max_num_reqs; i += PT) out.ctx_cu[i] = (int32_t)carry;
     for (int64_t i = R + tid; i <= p.max_num_reqs; i += PT) out.query_start_loc[i] = R * nqpr;
     for (int64_t i = R + tid; i < p.max_num_reqs; i += PT) out.seq_lens[i] = 0;
     for (int64_t i = (int64_t)R * nspec + tid; i < (int64_t)p.max_num_reqs * nspec; i += PT) {

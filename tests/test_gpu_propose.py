@@ -58,9 +58,9 @@ def _hand_batch(sample_from_anchor=False, max_model_len=100):
                 mask_token_id=-5, sample_from_anchor=sample_from_anchor)
 
 
-def _random_batch(seed, sample_from_anchor):
+def _random_batch(seed, sample_from_anchor, num_reqs=None):
     rng = np.random.default_rng(seed)
-    r = int(rng.integers(1, 41))
+    r = int(rng.integers(1, 41)) if num_reqs is None else num_reqs
     nqpr = int(rng.integers(1, 17))
     if not sample_from_anchor:
         nqpr = max(nqpr, 2)
@@ -107,6 +107,16 @@ def test_prepare_inputs_random(seed):
     print(f"case prepare random seed={seed} anchor={anchor}", flush=True)
     b = _random_batch(100 + seed, anchor)
     _assert_prep_equal(_run_prep(b), O.prepare_dflash_inputs(**b), f"seed {seed}")
+
+
+@pytest.mark.parametrize("num_reqs", [256, 600])
+def test_prepare_inputs_many_requests(num_reqs):
+    # the cumulative context lengths are scanned 256 requests at a time: a
+    # full chunk, then several chunks with a ragged tail
+    from oracle import dflash_oracle as O
+    print(f"case prepare many requests R={num_reqs}", flush=True)
+    b = _random_batch(500 + num_reqs, num_reqs % 2 == 0, num_reqs=num_reqs)
+    _assert_prep_equal(_run_prep(b), O.prepare_dflash_inputs(**b), f"R={num_reqs}")
 
 
 @pytest.mark.parametrize("shape", [(7, 256, 3), (128, 512, 5), (300, 128, 2), (64, 2048, 6)])
