@@ -20,6 +20,8 @@
 //                         bytes) K is split so that every CU streams a share of
 //                         the weight; the slices then write f32 partial tiles.
 //   split_sum_kernel      sums the K-slice partials and rounds to bf16.
+//   split_sum_krope_kernel  the same sum for a few context rows' stacked
+//                         [K | V] product, plus the K heads' k-norm and RoPE.
 // Output columns go to up to three row-major destinations (q | k | v).
 #include <algorithm>
 #include <mutex>
@@ -361,6 +363,105 @@ __global__ __launch_bounds__(256) void split_sum_kernel(const float* __restrict_
   }
 }
 
+// Context K/V rows (the stacked [K | V] product of a propose step's appended
+// rows): the K-slice partials summed in slice order and rounded to bf16, as
+// split_sum_kernel stores them, and for the K heads then the per-head k-norm
+// (RMSNorm over the 128 dims) and NeoX RoPE at the row's position, as
+// qk_norm_rope_kernel applies them to those stored values; one launch instead
+// of two. One head vector per 16 lanes: lane s holds dims [4s, 4s + 4) and
+// their rotation partners [64 + 4s, 64 + 4s + 4).
+constexpr int KR_DH = 128;
+__global__ __launch_bounds__(256) void split_sum_krope_kernel(
+    const float* __restrict__ part, int32_t nsplit, int64_t T, int32_t hkv, bf16* __restrict__ k_out,
+    bf16* __restrict__ v_out, const float* __restrict__ knw, const int32_t* __restrict__ pos,
+    const float2* __restrict__ table, int32_t max_pos, float eps) {
+  // every argument in one batch of scalar loads (no dependent argument reads)
+  asm volatile("" ::"s"(part), "s"(nsplit), "s"(T), "s"(hkv), "s"(k_out), "s"(v_out), "s"(knw),
+               "s"(pos), "s"(table), "s"(max_pos), "s"(eps));
+  constexpr int LANES = KR_DH / 8;
+  constexpr int HALF = KR_DH / 2;
+  const int s = (threadIdx.x & 63) % LANES;
+  const int64_t vec = ((int64_t)blockIdx.x * 256 + threadIdx.x) / LANES;  // 256-thread blocks
+  const int32_t heads = 2 * hkv;
+  const int32_t N = heads * KR_DH;
+  const bool valid = vec < T * heads;  // shared by the 16 lanes of a vector
+  const int64_t t = valid ? vec / heads : 0;
+  const int32_t h = valid ? (int32_t)(vec % heads) : 0;
+  const bool is_k = h < hkv;
+  // The K heads' operands (position, then its cos/sin, and the k-norm
+  // weights) are loaded ahead of the partials, so that their round trips
+  // overlap the partials' instead of following them.
+  float4 c01 = make_float4(0.f, 0.f, 0.f, 0.f), c23 = c01, w0 = c01, w1 = c01;
+  if (valid && is_k) {
+    int32_t p = pos[t];
+    p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+    const float4* cs4 = reinterpret_cast<const float4*>(table + (int64_t)p * HALF + 4 * s);
+    c01 = cs4[0];
+    c23 = cs4[1];
+    w0 = *reinterpret_cast<const float4*>(knw + 4 * s);
+    w1 = *reinterpret_cast<const float4*>(knw + HALF + 4 * s);
+  }
+  float x0[4] = {0.f, 0.f, 0.f, 0.f}, x1[4] = {0.f, 0.f, 0.f, 0.f};
+  if (valid) {
+    const int32_t c0 = h * KR_DH + 4 * s;
+    for (int32_t k0 = 0; k0 < nsplit; k0 += SB) {
+      f32x4 a[SB], b[SB];
+#pragma unroll
+      for (int kk = 0; kk < SB; ++kk) {
+        const int32_t k = min(k0 + kk, nsplit - 1);
+        const float* p = part + ((int64_t)k * T + t) * N + c0;
+        a[kk] = *reinterpret_cast<const f32x4*>(p);
+        b[kk] = *reinterpret_cast<const f32x4*>(p + HALF);
+      }
+#pragma unroll
+      for (int kk = 0; kk < SB; ++kk) {
+        if (k0 + kk < nsplit) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            x0[e] += a[kk][e];
+            x1[e] += b[kk][e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x0[e] = bf2f(f2bf(x0[e]));
+      x1[e] = bf2f(f2bf(x1[e]));
+    }
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) ss += x0[e] * x0[e] + x1[e] * x1[e];
+  ss = group_sum<LANES>(ss);
+  const float inv = 1.0f / sqrtf(ss * (1.0f / KR_DH) + eps);
+  if (!valid) return;
+  bf16x4 o0, o1;
+  bf16* dst;
+  if (!is_k) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      o0[e] = f2bf(x0[e]);
+      o1[e] = f2bf(x1[e]);
+    }
+    dst = v_out + (t * hkv + (h - hkv)) * KR_DH;
+  } else {
+    const float cs[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
+    const float wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float av = x0[e] * inv * wa[e];
+      const float bv = x1[e] * inv * wb[e];
+      const float c = cs[2 * e], sn = cs[2 * e + 1];
+      o0[e] = f2bf(av * c - bv * sn);
+      o1[e] = f2bf(bv * c + av * sn);
+    }
+    dst = k_out + (t * hkv + h) * KR_DH;
+  }
+  *reinterpret_cast<bf16x4*>(dst + 4 * s) = o0;
+  *reinterpret_cast<bf16x4*>(dst + HALF + 4 * s) = o1;
+}
+
 struct ProjPlan {
   int64_t mtiles;
   int32_t bn, ntiles, nsplit, ksteps;
@@ -409,7 +510,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 // from w); n1 must be a multiple of the tile width.
 hipError_t launch_proj(const bf16* a, const bf16* w, int64_t T, int32_t N, int32_t K,
                        const ProjPlan& pl, float* part, const OutSegs& out, hipStream_t s,
-                       const bf16* w2 = nullptr, int32_t n1 = 0) {
+                       const bf16* w2 = nullptr, int32_t n1 = 0, bool sum_slices = true) {
   // The LDS limit is a per-function setting: raised once per device, not per
   // launch (stream capture then sees only the launches).
   static std::once_flag once[64];
@@ -433,7 +534,7 @@ hipError_t launch_proj(const bf16* a, const bf16* w, int64_t T, int32_t N, int32
   else
     hipLaunchKernelGGL(proj_gemm_kernel<64>, dim3((unsigned)blocks), dim3(GNT), GemmShape<64>::LDS,
                        s, g);
-  if (pl.nsplit > 1) {
+  if (pl.nsplit > 1 && sum_slices) {
     const int64_t items = T * (N / 8);
     const int64_t sblocks = std::min<int64_t>((items + 255) / 256, 4096);
     hipLaunchKernelGGL(split_sum_kernel, dim3((unsigned)sblocks), dim3(256), 0, s,
@@ -535,6 +636,17 @@ hipError_t launch_context_kv_rows(const void* hidden, const float* hnw, const vo
   o.ptr[0] = (bf16*)k_out; o.ptr[1] = o.ptr[2] = (bf16*)v_out;
   o.stride[0] = o.stride[1] = o.stride[2] = n;
   o.begin[0] = 0; o.begin[1] = n; o.begin[2] = o.begin[3] = 2 * n;
+  if (pl.nsplit > 1 && dh == KR_DH) {
+    // the slice sum also applies the k-norm and RoPE to the K heads
+    hipError_t e = launch_proj(normed, (const bf16*)wk, T, 2 * n, hidden_size, pl, part, o, s,
+                               (const bf16*)wv, n, /*sum_slices=*/false);
+    if (e != hipSuccess) return e;
+    const int64_t threads = T * 2 * hkv * (KR_DH / 8);
+    hipLaunchKernelGGL(split_sum_krope_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                       s, (const float*)part, pl.nsplit, T, hkv, (bf16*)k_out, (bf16*)v_out, knw,
+                       pos, reinterpret_cast<const float2*>(table), max_pos, eps);
+    return hipGetLastError();
+  }
   hipError_t e = launch_proj(normed, (const bf16*)wk, T, 2 * n, hidden_size, pl, part, o, s,
                              (const bf16*)wv, n);
   if (e != hipSuccess) return e;

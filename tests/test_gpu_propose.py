@@ -275,8 +275,11 @@ def test_propose_flow_two_steps():
 
 
 # (the last case: 128-wide tiles, K's and V's weights as the two halves of N)
+# (hidden 256 plans one K slice: the GEMM writes K and V itself and the
+# q/k-norm kernel follows; the others sum split partials in the kernel that
+# also applies the k-norm and RoPE)
 @pytest.mark.parametrize("rows,hkv,h", [(1, 2, 512), (37, 2, 512), (255, 2, 512), (37, 4, 512),
-                                        (37, 16, 8192)])
+                                        (37, 16, 8192), (37, 2, 256)])
 def test_context_kv_few_rows_vs_oracle(rows, hkv, h):
     # calls of fewer than 256 rows (a step's appended rows) take the
     # projection-GEMM path (K and V in one product over the two weights);
