@@ -286,8 +286,11 @@ dflash_status dflash_kv_scatter(dflash_dtype dtype, const void* k_src, const voi
  * its verified rows) round the normed rows to bf16, run the split-K projection
  * GEMM and then the k-norm + RoPE (and need H <= 8192). Each output row
  * depends only on its own input row: splitting the rows across calls of at
- * least 256 rows each (or of fewer than 256 rows each) gives bitwise identical
- * results; the two forms agree within bf16 rounding.
+ * least 256 rows each gives bitwise identical results. Calls of fewer rows
+ * sum the partials of a split over H whose slice count follows from the
+ * number of 128-row tiles (at H = 4096 and Hkv = 8: 8 slices for up to 128
+ * rows, 4 for 129 to 255), so such calls give identical bits when they plan
+ * the same split; all forms agree within bf16 rounding.
  */
 size_t dflash_context_kv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_kv_heads,
                                         int32_t head_dim);

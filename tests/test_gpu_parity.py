@@ -293,6 +293,32 @@ def test_fused_rejections(dflash):
     assert e.value.status == dflash.DFLASH_ERR_UNSUPPORTED
 
 
+def test_context_kv_few_row_chunks_bitwise(dflash):
+    # calls of fewer than 256 rows with the same split plan (hidden 512: two
+    # K slices at any row count): each row's bits do not depend on the call
+    print("case context_kv few-row chunks", flush=True)
+    wl = make_workload("ctx_kv", num_reqs=2, ctx_len=700, hidden=512)
+    dp = DevicePath(wl)
+    rows = 200
+
+    def call(lo, hi):
+        k = torch.empty_like(dp.k_ctx[lo:hi])
+        v = torch.empty_like(dp.v_ctx[lo:hi])
+        ws = dflash.alloc_workspace(dflash.dflash_context_kv_workspace_size(hi - lo, wl.hidden_size,
+                                                                            wl.hkv, wl.dh))
+        dflash.dflash_context_kv(dp.hidden[lo:hi].contiguous(), dp.hidden_norm_w, dp.w_k, dp.w_v,
+                                 dp.k_norm_w, dp.ctx_pos[lo:hi].contiguous(), wl.hkv, wl.dh, wl.eps,
+                                 dp.rope, k, v, ws)
+        torch.cuda.synchronize()
+        return k, v
+
+    k_all, v_all = call(0, rows)
+    for lo, hi in ((0, 37), (37, 150), (150, rows)):
+        k, v = call(lo, hi)
+        assert torch.equal(k.view(torch.int16), k_all[lo:hi].view(torch.int16)), f"K rows {lo}:{hi}"
+        assert torch.equal(v.view(torch.int16), v_all[lo:hi].view(torch.int16)), f"V rows {lo}:{hi}"
+
+
 def test_context_kv_row_chunks_bitwise(dflash):
     # each output row depends only on its own hidden row: two calls over row
     # chunks (the second not aligned to the GEMM's 256-row blocks) give bitwise
