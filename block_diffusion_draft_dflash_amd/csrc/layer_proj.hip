@@ -36,16 +36,16 @@ constexpr int GBM = 128;  // output rows per workgroup tile
 constexpr int GBK = 64;   // K per ring stage (two MFMA k-steps of 32)
 constexpr int GNT = 256;  // threads (4 waves; wave w owns rows 32 w .. 32 w + 31)
 constexpr int A_TILE = GBM * GBK;
-// Two tile shapes: 128 x 64 (72 KB of LDS, two workgroups per CU) and
-// 128 x 128 (96 KB, one per CU) for wide outputs, both with 3 stages (2 in
-// flight; with the non-temporal weight copies the 128 x 128 tile measured
-// faster with 3 stages than with 4 or 5, and slower with 2).
+// Two tile shapes: 128 x 64 with 4 stages and 128 x 128 with 3 stages (both
+// 96 KB of LDS, one workgroup per CU) for wide outputs. With the
+// non-temporal weight copies these depths measured fastest: the wide tile
+// with 3 stages against 2, 4 or 5, the narrow one with 4 against 3 or 5.
 // Each stage copies the activation slice (A) next to the weight slice (W);
 // the A slice is the same for every column tile, so a wider tile spends less
 // of the bytes a CU keeps in flight on it.
 template <int BN>
 struct GemmShape {
-  static constexpr int NS = 3;                               // ring stages (NS - 1 in flight)
+  static constexpr int NS = BN == 128 ? 3 : 4;               // ring stages (NS - 1 in flight)
   static constexpr int W_TILE = BN * GBK;
   static constexpr int STAGE = A_TILE + W_TILE;              // bf16 elements per stage
   static constexpr int WCP = BN / 32;                        // W copies per wave per stage
