@@ -1,29 +1,39 @@
 #!/usr/bin/env python3
 """Benchmark of the DFlash draft block-attention hot path on one MI355X.
 
-One step = one pass of the path over one synthetic batch: the per-head q/k
-RMSNorm + NeoX RoPE of the block rows and the block attention over
-[context; block], as one ``dflash_block_attention`` call with the fused
-prologue (work-unit lookup, norm + RoPE, MFMA attention, split merge).
-``--unfused`` runs ``dflash_qk_norm_rope`` in place first and the attention
-on the normed rows (two calls). The context keys are prepared once
-before timing (``dflash_context_kv`` / K-only ``dflash_qk_norm_rope``), as a
-serving engine does when it appends context rows.
+One step = one draft step of the path over one synthetic batch whose context
+keys and values are already resident: the per-head q/k RMSNorm + NeoX RoPE of
+the block rows and the block attention over [context; block], as one
+``dflash_block_attention`` call with the fused prologue (work-unit lookup,
+norm + RoPE, MFMA attention, split merge). ``--unfused`` runs
+``dflash_qk_norm_rope`` in place first and the attention on the normed rows
+(two calls).
 
-Default workload: the Qwen3-8B-shaped draft layer (8 requests, context
-lengths uniform in [512, 2048], 16 block rows, Hq=32, Hkv=8, Dh=128, bf16,
-bidirectional). Inputs are resident in HBM before timing; ``--rotate`` copies
-of the batch are cycled so that the 256 MB Infinity Cache cannot serve the
-re-reads; the steps are replayed from a HIP graph.
+Default workload: ``ctx_kv`` -- 4 requests of 32768 context rows given as
+hidden states [131072, 4096]; ``dflash_context_kv`` (hidden RMSNorm, K/V
+projection, k-norm, RoPE) turns them into the context K/V caches before the
+timed steps, as a serving engine does when it appends context rows, and is
+timed in the same run (``context_kv``, against the bf16 MFMA peak), as is one
+whole pass of precompute + attention (``full_pass``). The other bf16
+workloads are timed in the same run as sub-records (``configs``); the draft
+layer around the attention and a whole captured propose step are timed on
+the Qwen3-8B-shaped batch.
 
-Prints one JSON line (rank 0).
+Inputs are resident in HBM before timing; enough copies of each batch are
+cycled that the 256 MB Infinity Cache cannot serve the re-reads; the steps
+are replayed from HIP graphs, exactly ``--steps`` of them in the timed
+region (whole-batch graphs plus single-step graphs for the remainder).
+
+Prints one JSON line.
 """
 from __future__ import annotations
 
 import argparse
 import hashlib
 import json
+import math
 import os
+import platform
 import sys
 import time
 
@@ -34,6 +44,8 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+ROTATE_BYTES = 512 << 20       # bytes the rotating copies of a batch span at least
+SUB_CONFIGS = ("qwen3_8b_draft", "large_decode", "swa")
 
 
 def algorithmic_cost(wl):
@@ -78,27 +90,106 @@ def committed_traffic(workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(wl, budget_s: float):
-    """Time the fp64 oracle on the host on the same batch (bounded sample)."""
-    from oracle import dflash_oracle as O
+def host_cpu():
+    """(threads the oracle's BLAS uses, cores this process may run on, CPU model)."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = os.cpu_count() or 1
-    _, k_ctx = O.qk_norm_rope(None, wl.k_ctx, None, wl.k_norm_w, wl.ctx_positions, wl.eps,
-                              wl.theta)
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except Exception:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    model = platform.processor() or "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    return threads, avail, model
+
+
+def _ctx_kv_sample(wl, rows):
+    """The oracle's context K/V of request 0's first ``rows`` context rows
+    (hidden-state workloads), with the lengths of that one-request sample."""
+    from oracle import dflash_oracle as O
+    from block_diffusion_draft_dflash_amd.workloads import bf16_bits_to_f32
+    c0 = int(wl.cu_ctx[0])
+    rows = min(rows, int(wl.ctx_lens[0]))
+    hid = bf16_bits_to_f32(wl.hidden[c0:c0 + rows])
+    t0 = time.perf_counter()
+    k_ctx, v_ctx = O.context_kv(hid, wl.hidden_norm_w, bf16_bits_to_f32(wl.w_k),
+                                bf16_bits_to_f32(wl.w_v), wl.k_norm_w,
+                                wl.ctx_positions[c0:c0 + rows], wl.hkv, wl.dh, wl.eps, wl.theta)
+    t_ckv = time.perf_counter() - t0
+    return k_ctx, v_ctx, rows, t_ckv
+
+
+def cpu_baseline(wl, budget_s: float, sample_reqs=None, ctx_rows=None):
+    """Time the fp64 oracle on the host on a bounded sample of the batch.
+
+    The sample is the first ``sample_reqs`` requests (all when None). For a
+    workload given as hidden states, the oracle first builds the sample's
+    context K/V itself (``context_kv`` on request 0's first ``ctx_rows`` rows,
+    timed apart) and the attention pass then runs over that request alone.
+    Returns a dict: seconds per attention pass, passes, threads, the sample's
+    algorithmic flops and query rows, a description, and the context-K/V
+    seconds and rows when built."""
+    from oracle import dflash_oracle as O
+    threads, avail, model = host_cpu()
+    if wl.hidden is not None:
+        k_ctx, v_ctx, rows, t_ckv = _ctx_kv_sample(wl, ctx_rows or int(wl.ctx_lens[0]))
+        b0, b1 = int(wl.cu_blk[0]), int(wl.cu_blk[1])
+        q, kb, vb, bpos = wl.q[b0:b1], wl.k_blk[b0:b1], wl.v_blk[b0:b1], wl.blk_positions[b0:b1]
+        cu_ctx, cu_blk = np.array([0, rows]), np.array([0, b1 - b0])
+        blk_lens = np.array([b1 - b0])
+        vis = np.array([rows + (b1 - b0)])
+        desc = (f"request 0 of {wl.num_reqs}: its first {rows} context rows through the oracle's "
+                f"context_kv ({t_ckv:.1f} s, not in the attention time), then q/k norm + RoPE + "
+                f"block attention of its {b1 - b0} block rows over them")
+        ckv = {"seconds": t_ckv, "rows": rows,
+               "flops": 2.0 * rows * wl.hidden_size * 2 * wl.hkv * wl.dh}
+    else:
+        nreq = wl.num_reqs if sample_reqs is None else min(sample_reqs, wl.num_reqs)
+        c1, b1 = int(wl.cu_ctx[nreq]), int(wl.cu_blk[nreq])
+        _, k_ctx = O.qk_norm_rope(None, wl.k_ctx[:c1], None, wl.k_norm_w, wl.ctx_positions[:c1],
+                                  wl.eps, wl.theta)
+        v_ctx = wl.v_ctx[:c1]
+        q, kb, vb, bpos = wl.q[:b1], wl.k_blk[:b1], wl.v_blk[:b1], wl.blk_positions[:b1]
+        cu_ctx, cu_blk = wl.cu_ctx[:nreq + 1], wl.cu_blk[:nreq + 1]
+        blk_lens = wl.blk_lens[:nreq]
+        vis = wl.visible_keys()[:nreq]
+        desc = (f"{nreq} of {wl.num_reqs} requests ({c1} context rows, {b1} block rows): "
+                "q/k norm + RoPE + block attention")
+        ckv = None
     reps = 0
     t0 = time.perf_counter()
     while True:
-        O.draft_block_attention(wl.q, wl.k_blk, wl.v_blk, wl.blk_positions, k_ctx, wl.v_ctx,
-                                wl.cu_ctx, wl.cu_blk, wl.q_norm_w, wl.k_norm_w, wl.eps, wl.theta,
-                                wl.scale, wl.causal, wl.window)
+        O.draft_block_attention(q, kb, vb, bpos, k_ctx, v_ctx, cu_ctx, cu_blk, wl.q_norm_w,
+                                wl.k_norm_w, wl.eps, wl.theta, wl.scale, wl.causal, wl.window)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
-    return el / reps, reps, threads
+    if wl.causal:
+        # per query its own visible keys (context + block rows at or before it, in the window)
+        flops = 0
+        for r in range(len(blk_lens)):
+            c = int(cu_ctx[r + 1] - cu_ctx[r])
+            for i in range(int(blk_lens[r])):
+                qi = c + i
+                lo = max(0, qi - wl.window + 1) if wl.window > 0 else 0
+                flops += qi + 1 - lo
+        flops *= wl.hq * 4 * wl.dh
+    else:
+        flops = int((blk_lens.astype(np.int64) * vis).sum()) * wl.hq * 4 * wl.dh
+    return {"seconds": el / reps, "passes": reps, "threads": threads, "cores_available": avail,
+            "cpu_model": model, "flops": flops, "query_rows": int(blk_lens.sum()),
+            "sample": desc, "context_kv": ckv}
 
 
 def device_copy_gbs(stream, mib=512, reps=5):
@@ -121,6 +212,163 @@ def device_copy_gbs(stream, mib=512, reps=5):
     t = e0.elapsed_time(e1) * 1e-3 / reps
     del src, dst
     return 2.0 * n / t / 1e9
+
+
+class StepRunner:
+    """Steps of the path over ``copies`` resident copies of one batch, replayed
+    from HIP graphs: one graph holds a step on every copy in turn, and one
+    graph per copy holds a single step, so that any number of steps runs
+    exactly (whole passes over the copies, then single steps)."""
+
+    def __init__(self, paths, fused, use_graph):
+        import torch
+        self.paths, self.fused, self.use_graph = paths, fused, use_graph
+        if not use_graph:
+            return
+        for i in range(len(paths)):          # warm the launch path before capture
+            self._step(i)
+        torch.cuda.synchronize()
+        self.g_all = {}
+        self.g_one = {}
+        for attn_only in (False, True):
+            if self.fused and attn_only:
+                self.g_all[True], self.g_one[True] = self.g_all[False], self.g_one[False]
+                break
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(len(paths)):
+                    self._step(i, attn_only)
+            self.g_all[attn_only] = g
+            ones = []
+            for i in range(len(paths)):
+                g1 = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g1):
+                    self._step(i, attn_only)
+                ones.append(g1)
+            self.g_one[attn_only] = ones
+        torch.cuda.synchronize()
+
+    def _step(self, i, attention_only=False):
+        p = self.paths[i]
+        if self.fused:
+            p.step_fused()          # the step is the attention call
+        elif attention_only:
+            p.attention()
+        else:
+            p.step()
+
+    def run(self, n, attention_only=False):
+        """Exactly n steps, cycling over the copies."""
+        n_copies = len(self.paths)
+        if not self.use_graph:
+            for i in range(n):
+                self._step(i % n_copies, attention_only)
+            return
+        whole, rest = divmod(n, n_copies)
+        for _ in range(whole):
+            self.g_all[attention_only].replay()
+        for i in range(rest):
+            self.g_one[attention_only][i].replay()
+
+
+def rotate_copies(wl, requested):
+    if requested > 0:
+        return requested
+    bytes_attn, _, _ = algorithmic_cost(wl)
+    return max(2, -(-ROTATE_BYTES // max(1, bytes_attn)))
+
+
+def time_attention(name, wl, args, stream, steps, warmup, min_sample_ms):
+    """Upload ``copies`` of the batch, prepare their context keys, and time
+    (a) exactly ``steps`` steps between synchronisations (the step time), and
+    (b) the attention call alone with HIP events on its stream over at least
+    ``min_sample_ms`` (the dominant kernel's average launch time)."""
+    import torch
+    from block_diffusion_draft_dflash_amd.pipeline import DevicePath
+
+    copies = rotate_copies(wl, args.rotate)
+    paths = [DevicePath(wl, split_keys=args.split_keys, host_lengths=not args.device_plan,
+                        paged=args.paged) for _ in range(copies)]
+    for p in paths:
+        p.prepare_context()
+    torch.cuda.synchronize()
+    fused = wl.dtype == "bf16" and not args.unfused
+    use_graph = not args.no_graph
+    runner = StepRunner(paths, fused, use_graph)
+
+    runner.run(warmup)
+    torch.cuda.synchronize()
+    # ---- timed region: exactly `steps` steps
+    t0 = time.perf_counter()
+    runner.run(steps)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / max(steps, 1)
+
+    # ---- the attention call alone, HIP events on its stream
+    est_us = max(ms_per_step * 1e3, 1.0)
+    n_attn = max(steps, int(math.ceil(min_sample_ms * 1e3 / est_us)))
+    n_attn = -(-n_attn // copies) * copies
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    ev0.record(stream)
+    runner.run(n_attn, attention_only=True)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    attn_us = ev0.elapsed_time(ev1) * 1e3 / n_attn
+
+    bytes_attn, flops_attn, bytes_pro = algorithmic_cost(wl)
+    achieved = bytes_attn / (attn_us * 1e-6) / 1e9
+    rec = {
+        "workload": name, "requests": wl.num_reqs, "context_rows": wl.total_ctx,
+        "block_rows": wl.total_blk, "hq": wl.hq, "hkv": wl.hkv, "dh": wl.dh,
+        "mask": ("causal, window %d" % wl.window) if wl.causal else "bidirectional",
+        "rotating_copies": copies, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "tflops": flops_attn / (ms_per_step * 1e-3) / 1e12,
+        "draft_query_tokens_per_s": wl.total_blk / (ms_per_step * 1e-3),
+        "attention_call_us": attn_us, "attention_calls_timed": n_attn,
+        "achieved_gbs": achieved, "frac_of_hbm_peak": achieved / HBM_PEAK_GBS,
+        "attention_bytes": bytes_attn, "attention_flops": flops_attn,
+        "prologue_bytes": bytes_pro, "fused": fused, "hip_graph": use_graph,
+    }
+    return rec, paths
+
+
+def time_context_kv(wl, path, stream, reps=5):
+    """The dflash_context_kv call (weight fold, fused GEMM + row rms + k-norm +
+    RoPE) with HIP events on its stream, against the dense bf16 MFMA peak, and
+    one whole pass of precompute then the attention step."""
+    import torch
+    path.prepare_context()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        path.prepare_context()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ckv_ms = e0.elapsed_time(e1) / reps
+    flops = 2.0 * wl.total_ctx * wl.hidden_size * (2 * wl.hkv * wl.dh)
+    tflops = flops / (ckv_ms * 1e-3) / 1e12
+    # algorithmic bytes: hidden rows in, weights in, K and V caches out
+    bytes_ckv = (wl.total_ctx * wl.hidden_size * 2 + 2 * wl.hkv * wl.dh * wl.hidden_size * 2
+                 + 2 * wl.total_ctx * wl.hkv * wl.dh * 2)
+    e0.record(stream)
+    for _ in range(reps):
+        path.prepare_context()
+        path.step_fused()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pass_ms = e0.elapsed_time(e1) / reps
+    return (
+        {"ms": ckv_ms, "tflops": tflops, "bound": "mfma", "peak_tflops": BF16_PEAK_TFLOPS,
+         "frac": tflops / BF16_PEAK_TFLOPS, "flops": flops, "bytes": bytes_ckv,
+         "rows": wl.total_ctx, "hidden": wl.hidden_size, "calls_timed": reps},
+        {"ms": pass_ms, "stages": "dflash_context_kv then dflash_block_attention (fused)",
+         "passes_timed": reps},
+    )
 
 
 def time_layer(wl, hidden, stream, use_graph, reps=60):
@@ -178,7 +426,7 @@ def time_layer(wl, hidden, stream, use_graph, reps=60):
     qkv_gbs = qkv_bytes / (qkv_us * 1e-6) / 1e9
     o_gbs = o_bytes / (o_us * 1e-6) / 1e9
     return {
-        "hidden": hidden, "weight_copies": copies,
+        "hidden": hidden, "weight_copies": copies, "block_rows": t,
         "block_qkv": {"us": qkv_us, "bytes": qkv_bytes, "achieved_gbs": qkv_gbs,
                       "frac": qkv_gbs / HBM_PEAK_GBS, "bound": "hbm"},
         "o_proj": {"us": o_us, "bytes": o_bytes, "achieved_gbs": o_gbs,
@@ -192,9 +440,9 @@ def time_draft_step(wl, hidden, taps, stream, reps=50):
     """A whole propose step of one draft layer on this batch's shape, replayed
     from one HIP graph: the integer preparation, fc combine of the verified
     rows' tapped features, their context K/V appended to a paged store,
-    block q/k/v, the paged attention (work split planned on the device) and
-    o_proj. Each request verifies one block of rows on top of its context."""
-    import numpy as np
+    block q/k/v, the paged attention (work split planned on the device, the
+    batch's mask flags) and o_proj. Each request verifies one block of rows on
+    top of its context."""
     import torch
     from block_diffusion_draft_dflash_amd.pipeline import DraftStep
 
@@ -202,7 +450,7 @@ def time_draft_step(wl, hidden, taps, stream, reps=50):
     rows = nqpr
     pages = (int(wl.ctx_lens.max()) + rows + 15) // 16 + 1
     ds = DraftStep(wl.num_reqs, nqpr, rows, hidden=hidden, taps=taps, hq=wl.hq, hkv=wl.hkv,
-                   dh=wl.dh, pages_per_req=pages, seed=11)
+                   dh=wl.dh, pages_per_req=pages, seed=11, causal=wl.causal, window=wl.window)
     rng = np.random.default_rng(12)
     pos = np.concatenate([np.arange(c, c + rows) for c in wl.ctx_lens.tolist()])
     rej = rng.integers(0, rows, size=wl.num_reqs)
@@ -239,10 +487,13 @@ def time_draft_step(wl, hidden, taps, stream, reps=50):
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1200)
-    ap.add_argument("--warmup", type=int, default=120)
-    ap.add_argument("--workload", default="qwen3_8b_draft")
-    ap.add_argument("--rotate", type=int, default=12, help="copies of the batch cycled per step")
+    ap.add_argument("--steps", type=int, default=600)
+    ap.add_argument("--warmup", type=int, default=60)
+    ap.add_argument("--workload", default="ctx_kv")
+    ap.add_argument("--rotate", type=int, default=0,
+                    help="copies of the batch cycled per step (0: enough to span 512 MiB)")
+    ap.add_argument("--min-sample-ms", type=float, default=30.0,
+                    help="GPU time the attention-call timing (HIP events) spans at least")
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--no-graph", action="store_true", help="launch eagerly instead of replaying a HIP graph")
     ap.add_argument("--unfused", action="store_true",
@@ -252,9 +503,13 @@ def main() -> int:
     ap.add_argument("--device-plan", action="store_true",
                     help="leave the work split to the kernels (no host copies of the lengths)")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of oracle time (0: skip)")
+    ap.add_argument("--sub-configs", default=",".join(SUB_CONFIGS),
+                    help="other workloads timed in the same run as sub-records ('' for none)")
     ap.add_argument("--layer-hidden", type=int, default=4096,
                     help="hidden size of the draft layer whose projections around the attention "
                          "(dflash_block_qkv, dflash_o_proj) are also timed (0: skip)")
+    ap.add_argument("--layer-workload", default="qwen3_8b_draft",
+                    help="the batch the draft layer and the propose step are timed on")
     ap.add_argument("--draft-step-taps", type=int, default=5,
                     help="target taps of the fc combine in the timed whole propose step (0: skip it)")
     ap.add_argument("--copy-calibration-mb", type=int, default=0,
@@ -266,10 +521,12 @@ def main() -> int:
         print(f"bench.py: the library runs on one GPU; --gpus {args.gpus} is not supported "
               "(sharding across GPUs is described, not built).", file=sys.stderr)
         return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
 
     import torch
     from block_diffusion_draft_dflash_amd import binding as B
-    from block_diffusion_draft_dflash_amd.pipeline import DevicePath
     from block_diffusion_draft_dflash_amd.workloads import make_workload
 
     if not torch.cuda.is_available():
@@ -284,138 +541,78 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    wl = make_workload(args.workload)
-    paths = [DevicePath(wl, split_keys=args.split_keys, host_lengths=not args.device_plan,
-                        paged=args.paged)
-             for _ in range(args.rotate)]
-    for p in paths:
-        p.prepare_context()
-    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
 
-    fused = wl.dtype == "bf16" and not args.unfused
+    wl = make_workload(args.workload)
+    head, paths = time_attention(args.workload, wl, args, stream, args.steps, args.warmup,
+                                 args.min_sample_ms)
 
-    def run_steps(n, attention_only=False):
-        for i in range(n):
-            p = paths[i % len(paths)]
-            if fused:
-                p.step_fused()          # the step is the attention call
-            elif attention_only:
-                p.attention()
-            else:
-                p.step()
-
-    per_graph = len(paths)
-    use_graph = not args.no_graph
-    if use_graph:
-        # warm the launch path (function attributes, code objects) before capture
-        run_steps(per_graph)
-        torch.cuda.synchronize()
-        g_step = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_step):
-            run_steps(per_graph)
-        g_attn = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g_attn):
-            run_steps(per_graph, attention_only=True)
-        torch.cuda.synchronize()
-
-        def steps(n, attention_only=False):
-            g = g_attn if attention_only else g_step
-            for _ in range(max(1, n // per_graph)):
-                g.replay()
-        steps_eff = max(1, args.steps // per_graph) * per_graph
-    else:
-        steps = run_steps
-        steps_eff = args.steps
-
-    steps(args.warmup)
+    ckv = full_pass = None
+    if wl.hidden is not None:
+        ckv, full_pass = time_context_kv(wl, paths[0], stream)
+    del paths
     torch.cuda.synchronize()
+    torch.cuda.empty_cache()
 
-    # ---- timed region: exactly steps_eff steps
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    steps(steps_eff)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / steps_eff
-
-    # ---- dominant kernel (block attention) average duration, HIP events on its stream
-    n_attn = steps_eff
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    ev0.record(stream)
-    steps(n_attn, attention_only=True)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    attn_us = ev0.elapsed_time(ev1) * 1e3 / (max(1, n_attn // per_graph) * per_graph
-                                            if use_graph else n_attn)
-
-    bytes_attn, flops_attn, bytes_pro = algorithmic_cost(wl)
-    # (skipped in a counter-calibration run, whose copy must be the only one)
-    copy_gbs = device_copy_gbs(stream) if args.copy_calibration_mb == 0 else None
-    step_s = ms_per_step * 1e-3
-    value = flops_attn / step_s / 1e12
-    tokens_per_s = wl.total_blk / step_s
-    achieved_gbs = bytes_attn / (attn_us * 1e-6) / 1e9
-    # the counters were taken on the default launch (packed store, fused
-    # prologue, host-planned split): another launch gets no traffic figure
+    # the dominant kernel's traffic, from the committed counter record: only
+    # for the default launch (packed store, fused prologue, host-planned split)
     default_launch = not (args.paged or args.unfused or args.device_plan or args.split_keys)
     traffic = committed_traffic(args.workload) if default_launch else None
+    copy_gbs = device_copy_gbs(stream) if args.copy_calibration_mb == 0 else None
 
-    # Context-K/V precompute (hidden-state workloads): the dflash_context_kv
-    # call (weight fold, row rms, fused GEMM + k-norm + RoPE), HIP events on
-    # its stream, against the dense bf16 MFMA peak.
-    ckv = None
-    if wl.hidden is not None:
-        p0 = paths[0]
-        p0.prepare_context()
+    subs = {}
+    for name in [s for s in args.sub_configs.split(",") if s and s != args.workload]:
+        swl = make_workload(name)
+        if swl.dtype != "bf16":
+            continue
+        rec, spaths = time_attention(name, swl, args, stream, max(args.steps, 120),
+                                     max(args.warmup, 12), args.min_sample_ms)
+        rec["traffic"] = committed_traffic(name) if default_launch else None
+        subs[name] = rec
+        del spaths
         torch.cuda.synchronize()
-        reps = 5
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(reps):
-            p0.prepare_context()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ckv_ms = e0.elapsed_time(e1) / reps
-        ckv_flops = 2.0 * wl.total_ctx * wl.hidden_size * (2 * wl.hkv * wl.dh)
-        ckv = {"ms": ckv_ms, "tflops": ckv_flops / (ckv_ms * 1e-3) / 1e12,
-               "peak_tflops": BF16_PEAK_TFLOPS,
-               "frac": ckv_flops / (ckv_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-               "flops": ckv_flops, "rows": wl.total_ctx, "hidden": wl.hidden_size}
+        torch.cuda.empty_cache()
 
-    layer = None
-    if args.layer_hidden > 0 and wl.dtype == "bf16" and not args.paged:
-        layer = time_layer(wl, args.layer_hidden, stream, use_graph)
-    draft_step = None
-    if (args.draft_step_taps > 0 and args.layer_hidden > 0 and wl.dtype == "bf16"
-            and not args.paged and wl.hidden is None):
-        draft_step = time_draft_step(wl, args.layer_hidden, args.draft_step_taps, stream)
+    layer = draft_step = None
+    if args.layer_hidden > 0 and not args.paged:
+        lwl = wl if args.layer_workload == args.workload else make_workload(args.layer_workload)
+        if lwl.dtype == "bf16":
+            layer = time_layer(lwl, args.layer_hidden, stream, not args.no_graph)
+            layer["workload"] = args.layer_workload
+            torch.cuda.empty_cache()
+            if args.draft_step_taps > 0:
+                draft_step = time_draft_step(lwl, args.layer_hidden, args.draft_step_taps, stream)
+                draft_step["workload"] = args.layer_workload
 
     cpu = None
     if args.cpu_budget > 0:
-        t_cpu, reps, threads = cpu_baseline(wl, args.cpu_budget)
+        cb = cpu_baseline(wl, args.cpu_budget, ctx_rows=None)
         cpu = {
-            "value": flops_attn / t_cpu / 1e12,
+            "value": cb["flops"] / cb["seconds"] / 1e12,
             "unit": "TFLOP/s",
-            "cores": threads,
+            "cores": cb["threads"],
             "kind": "oracle",
-            "sample": (f"fp64 numpy oracle, q/k norm + RoPE + block attention over the full "
-                       f"{args.workload} batch ({wl.num_reqs} requests, {wl.total_ctx} context rows, "
-                       f"{wl.total_blk} block rows), {reps} passes in {t_cpu * reps:.1f} s"),
-            "ms_per_step": t_cpu * 1e3,
-            "draft_query_tokens_per_s": wl.total_blk / t_cpu,
+            "sample": (f"fp64 numpy oracle on {cb['sample']}; {cb['passes']} passes in "
+                       f"{cb['seconds'] * cb['passes']:.1f} s"),
+            "ms_per_step": cb["seconds"] * 1e3,
+            "draft_query_tokens_per_s": cb["query_rows"] / cb["seconds"],
+            "cpu_model": cb["cpu_model"],
+            "cores_available": cb["cores_available"],
         }
+        if cb["context_kv"] is not None:
+            c = cb["context_kv"]
+            cpu["context_kv"] = {"rows": c["rows"], "seconds": c["seconds"],
+                                 "tflops": c["flops"] / c["seconds"] / 1e12}
 
+    bytes_attn = head["attention_bytes"]
     rec = {
         "metric": "block-attention TFLOP/s and draft query tokens/s; % of MI355X roofline",
-        "value": value,
+        "value": head["tflops"],
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": steps_eff,
+        "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
+        "ms_per_step": head["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -427,35 +624,39 @@ def main() -> int:
             "context_rows": wl.total_ctx,
             "block_rows": wl.total_blk,
             "hq": wl.hq, "hkv": wl.hkv, "dh": wl.dh,
-            "mask": ("causal, window %d" % wl.window) if wl.causal else "bidirectional",
-            "rotating_copies": len(paths),
-            "hip_graph": use_graph,
-            "fused_qk_norm_rope": fused,
+            "hidden": wl.hidden_size or None,
+            "mask": head["mask"],
+            "rotating_copies": head["rotating_copies"],
+            "hip_graph": head["hip_graph"],
+            "fused_qk_norm_rope": head["fused"],
             "work_split": "device-planned" if args.device_plan else "host-planned",
             "context_store": "paged (16-row pages)" if args.paged else "packed",
         },
-        "draft_query_tokens_per_s": tokens_per_s,
+        "draft_query_tokens_per_s": head["draft_query_tokens_per_s"],
         "roofline": {
             "bound": "hbm",
             "kernel": ("dflash_block_attention%s call = block_attn_bf16_kernel%s + "
                        "block_attn_merge_kernel" % ("_paged" if args.paged else "",
-                                                    " (fused q/k norm + RoPE)" if fused else "")),
-            "achieved": achieved_gbs,
+                                                    " (fused q/k norm + RoPE)" if head["fused"] else "")),
+            "achieved": head["achieved_gbs"],
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
-            "frac": achieved_gbs / HBM_PEAK_GBS,
+            "frac": head["frac_of_hbm_peak"],
             "traffic": traffic,
             "algorithmic_bytes_per_launch": bytes_attn,
-            "avg_launch_us": attn_us,
+            "avg_launch_us": head["attention_call_us"],
+            "launches_timed": head["attention_calls_timed"],
             "achievable_copy_gbs": copy_gbs,
-            "frac_of_copy": achieved_gbs / copy_gbs if copy_gbs else None,
+            "frac_of_copy": head["achieved_gbs"] / copy_gbs if copy_gbs else None,
         },
         "cpu_baseline": cpu,
         "context_kv": ckv,
+        "full_pass": full_pass,
+        "configs": subs,
         "draft_layer": layer,
         "draft_step": draft_step,
-        "algorithmic": {"attention_bytes": bytes_attn, "attention_flops": flops_attn,
-                        "prologue_bytes": bytes_pro},
+        "algorithmic": {"attention_bytes": bytes_attn, "attention_flops": head["attention_flops"],
+                        "prologue_bytes": head["prologue_bytes"]},
     }
     print(json.dumps(rec), flush=True)
     return 0

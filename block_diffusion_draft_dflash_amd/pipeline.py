@@ -268,11 +268,13 @@ class DraftStep:
 
     Each request verifies ``rows_per_req`` rows per step; the block rows'
     hidden states (the embedding of the anchor + mask tokens, outside this
-    library) are a fixed synthetic input."""
+    library) are a fixed synthetic input. ``causal`` / ``window`` are the
+    layer's mask flags (a sliding-window layer is causal with a window)."""
 
     def __init__(self, num_reqs: int, nqpr: int, rows_per_req: int, hidden: int = 256,
                  taps: int = 3, hq: int = 4, hkv: int = 2, dh: int = 128, pages_per_req: int = 16,
-                 seed: int = 0, device: str = "cuda", eps: float = 1e-6, theta: float = 1e6):
+                 seed: int = 0, device: str = "cuda", eps: float = 1e-6, theta: float = 1e6,
+                 causal: bool = False, window: int = 0):
         rng = np.random.default_rng(seed)
         self.r, self.nqpr, self.rows = num_reqs, nqpr, rows_per_req
         self.h, self.taps, self.hq, self.hkv, self.dh = hidden, taps, hq, hkv, dh
@@ -328,7 +330,8 @@ class DraftStep:
         self.attn = torch.empty_like(self.q)
         self.o = torch.empty((t, hidden), dtype=bf, device=dev)
         self.params = B.make_block_attn_params(num_reqs, hq, hkv, dh, B.DFLASH_BF16,
-                                               num_reqs * pages_per_req * page, t, nqpr, dh ** -0.5)
+                                               num_reqs * pages_per_req * page, t, nqpr, dh ** -0.5,
+                                               causal=causal, window=window)
         self.pg = B.make_paged_ctx(self.block_table, self.pages)
         self.pro = B.make_qk_prologue(self.qnw, self.knw, self.outs["query_positions"], self.rope, eps)
         self.ws_fc = B.alloc_workspace(B.dflash_fc_combine_workspace_size(ntgt, hidden, taps), dev)

@@ -809,3 +809,171 @@ def test_fc_combine_and_bf16_round_pins():
     np.testing.assert_allclose(O.fc_combine(aux, w),
                                torch.nn.functional.linear(torch.from_numpy(aux), torch.from_numpy(w)).numpy(),
                                rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------- composed functions
+# draft_block_attention and draft_layer_attention are the reference of every
+# GPU attention parity test. They are pinned here with distinct, non-unit q,
+# k and input-norm weights and non-trivial positions against a composition of
+# independent pieces: torch's fp64 rms_norm and linear, RoPE in its complex
+# form (x_i + i x_{i+Dh/2}) e^{i p theta^(-2i/Dh)}, and torch's
+# scaled_dot_product_attention with an explicit mask over [context; block].
+
+def _ref_rope_complex(x, pos, theta):
+    x = np.asarray(x, np.float64)
+    half = x.shape[-1] // 2
+    inv = float(theta) ** (-2.0 * np.arange(half) / x.shape[-1])
+    z = (x[..., :half] + 1j * x[..., half:]) * np.exp(1j * np.outer(pos, inv))[:, None, :]
+    return np.concatenate([z.real, z.imag], axis=-1)
+
+
+def _ref_head_norm(x, w, eps):
+    t = torch.from_numpy(np.asarray(x, np.float64))
+    return torch.nn.functional.rms_norm(t, (t.shape[-1],), torch.from_numpy(np.asarray(w, np.float64)),
+                                        eps=eps).numpy()
+
+
+def _ref_sdpa(qh, kh, vb, kc, vc, cu_c, cu_b, scale, causal, window):
+    out = np.zeros_like(qh)
+    for r in range(len(cu_b) - 1):
+        c0, c1, b0, b1 = int(cu_c[r]), int(cu_c[r + 1]), int(cu_b[r]), int(cu_b[r + 1])
+        n, bl = c1 - c0 + b1 - b0, b1 - b0
+        keys = torch.from_numpy(np.concatenate([kc[c0:c1], kh[b0:b1]])).permute(1, 0, 2).contiguous()
+        vals = torch.from_numpy(np.concatenate([vc[c0:c1], vb[b0:b1]])).permute(1, 0, 2).contiguous()
+        qq = torch.from_numpy(qh[b0:b1]).permute(1, 0, 2).contiguous()
+        qi = torch.arange(bl).reshape(-1, 1) + (c1 - c0)
+        kj = torch.arange(n).reshape(1, -1)
+        mask = torch.ones(bl, n, dtype=torch.bool)
+        if causal:
+            mask = kj <= qi
+            if window > 0:
+                mask &= (qi - kj) < window
+        o = torch.nn.functional.scaled_dot_product_attention(qq, keys, vals, attn_mask=mask,
+                                                             scale=scale, enable_gqa=True)
+        out[b0:b1] = o.permute(1, 0, 2).numpy()
+    return out
+
+
+def _comp_batch(seed):
+    rng = np.random.default_rng(seed)
+    hq, hkv, d = 6, 2, 8
+    cu_c, cu_b = np.array([0, 11, 11, 30]), np.array([0, 4, 9, 12])
+    t, c = int(cu_b[-1]), int(cu_c[-1])
+    # block positions not at the context's end, one request's reversed
+    pos = np.concatenate([np.arange(int(cu_c[r + 1] - cu_c[r]), int(cu_c[r + 1] - cu_c[r] + cu_b[r + 1] - cu_b[r]))
+                          + 5 * r for r in range(3)])
+    pos[4:9] = pos[4:9][::-1]
+    return dict(
+        hq=hq, hkv=hkv, d=d, cu_c=cu_c, cu_b=cu_b, pos=pos,
+        q=rng.standard_normal((t, hq, d)) * 2.0, kb=rng.standard_normal((t, hkv, d)) * 0.5,
+        vb=rng.standard_normal((t, hkv, d)), kc=rng.standard_normal((c, hkv, d)),
+        vc=rng.standard_normal((c, hkv, d)),
+        wq=rng.uniform(0.5, 1.5, d), wk=rng.uniform(0.5, 1.5, d) + 0.75,
+        theta=500.0, eps=1e-6, scale=0.41, rng=rng)
+
+
+def _comp_ns(**over):
+    base = dict(draft_block_attention=O.draft_block_attention,
+                draft_layer_attention=O.draft_layer_attention)
+    base.update(over)
+    return types.SimpleNamespace(**base)
+
+
+def cpin_draft_block_attention(X):
+    b = _comp_batch(77)
+    for causal, window in ((False, 0), (True, 0), (True, 6)):
+        out, qh, kh = X.draft_block_attention(b["q"], b["kb"], b["vb"], b["pos"], b["kc"], b["vc"],
+                                              b["cu_c"], b["cu_b"], b["wq"], b["wk"], b["eps"],
+                                              b["theta"], b["scale"], causal, window)
+        rq = _ref_rope_complex(_ref_head_norm(b["q"], b["wq"], b["eps"]), b["pos"], b["theta"])
+        rk = _ref_rope_complex(_ref_head_norm(b["kb"], b["wk"], b["eps"]), b["pos"], b["theta"])
+        np.testing.assert_allclose(qh, rq, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(kh, rk, rtol=1e-12, atol=1e-12)
+        ref = _ref_sdpa(rq, rk, b["vb"], b["kc"], b["vc"], b["cu_c"], b["cu_b"], b["scale"],
+                        causal, window)
+        np.testing.assert_allclose(out, ref, rtol=1e-11, atol=1e-12)
+
+
+def cpin_draft_layer_attention(X):
+    b = _comp_batch(78)
+    rng = b["rng"]
+    hq, hkv, d = b["hq"], b["hkv"], b["d"]
+    h, t = 20, int(b["cu_b"][-1])
+    x, res_in = rng.standard_normal((t, h)), rng.standard_normal((t, h))
+    w_in = rng.uniform(0.5, 1.5, h)
+    w_qkv = rng.standard_normal(((hq + 2 * hkv) * d, h)) * 0.4
+    w_o = rng.standard_normal((h, hq * d)) * 0.3
+    for causal, window in ((False, 0), (True, 5)):
+        o, res, q, k, v, attn = X.draft_layer_attention(
+            x, res_in, w_in, w_qkv, w_o, b["pos"], b["kc"], b["vc"], b["cu_c"], b["cu_b"], b["wq"],
+            b["wk"], hq, hkv, d, b["eps"], b["theta"], b["scale"], causal, window)
+        tt = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+        r_res = x + res_in
+        normed = torch.nn.functional.rms_norm(tt(r_res), (h,), tt(w_in), eps=b["eps"])
+        qkv = torch.nn.functional.linear(normed, tt(w_qkv)).numpy()
+        rq = qkv[:, :hq * d].reshape(t, hq, d)
+        rk = qkv[:, hq * d:(hq + hkv) * d].reshape(t, hkv, d)
+        rv = qkv[:, (hq + hkv) * d:].reshape(t, hkv, d)
+        qh = _ref_rope_complex(_ref_head_norm(rq, b["wq"], b["eps"]), b["pos"], b["theta"])
+        kh = _ref_rope_complex(_ref_head_norm(rk, b["wk"], b["eps"]), b["pos"], b["theta"])
+        ra = _ref_sdpa(qh, kh, rv, b["kc"], b["vc"], b["cu_c"], b["cu_b"], b["scale"], causal, window)
+        ro = torch.nn.functional.linear(tt(ra.reshape(t, hq * d)), tt(w_o)).numpy()
+        np.testing.assert_array_equal(res, r_res)
+        for got, ref in ((q, rq), (k, rk), (v, rv)):
+            np.testing.assert_allclose(got, ref, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(attn, ra, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(o, ro, rtol=1e-11, atol=1e-12)
+
+
+COMPOSED_PINS = [cpin_draft_block_attention, cpin_draft_layer_attention]
+
+
+@pytest.mark.parametrize("pin", COMPOSED_PINS, ids=[p.__name__ for p in COMPOSED_PINS])
+def test_composed_oracle_pin(pin):
+    pin(_comp_ns())
+
+
+def _cmut_block_qk_weights_swapped(q, kb, vb, pos, kc, vc, cu_c, cu_b, wq, wk, *rest):
+    return O.draft_block_attention(q, kb, vb, pos, kc, vc, cu_c, cu_b, wk, wq, *rest)
+
+
+def _cmut_block_no_rope(q, kb, vb, pos, kc, vc, cu_c, cu_b, *rest):
+    return O.draft_block_attention(q, kb, vb, np.zeros_like(pos), kc, vc, cu_c, cu_b, *rest)
+
+
+def _cmut_block_q_weight_for_both(q, kb, vb, pos, kc, vc, cu_c, cu_b, wq, wk, *rest):
+    return O.draft_block_attention(q, kb, vb, pos, kc, vc, cu_c, cu_b, wq, wq, *rest)
+
+
+def _cmut_layer_qk_weights_swapped(x, r, w_in, w_qkv, w_o, pos, kc, vc, cu_c, cu_b, wq, wk, *rest):
+    return O.draft_layer_attention(x, r, w_in, w_qkv, w_o, pos, kc, vc, cu_c, cu_b, wk, wq, *rest)
+
+
+def _cmut_layer_unit_input_norm(x, r, w_in, *rest):
+    return O.draft_layer_attention(x, r, np.ones_like(w_in), *rest)
+
+
+def _cmut_layer_no_residual(x, r, *rest):
+    return O.draft_layer_attention(x, None, *rest)
+
+
+COMPOSED_MUTANTS = {
+    "block_q_k_norm_weights_swapped": dict(draft_block_attention=_cmut_block_qk_weights_swapped),
+    "block_rope_at_position_zero": dict(draft_block_attention=_cmut_block_no_rope),
+    "block_q_norm_weight_on_k": dict(draft_block_attention=_cmut_block_q_weight_for_both),
+    "layer_q_k_norm_weights_swapped": dict(draft_layer_attention=_cmut_layer_qk_weights_swapped),
+    "layer_input_norm_weight_dropped": dict(draft_layer_attention=_cmut_layer_unit_input_norm),
+    "layer_residual_dropped": dict(draft_layer_attention=_cmut_layer_no_residual),
+}
+
+
+@pytest.mark.parametrize("name", sorted(COMPOSED_MUTANTS))
+def test_composed_pins_catch_planted_mistakes(name):
+    ns = _comp_ns(**COMPOSED_MUTANTS[name])
+    failed = []
+    for pin in COMPOSED_PINS:
+        try:
+            pin(ns)
+        except (AssertionError, ValueError):
+            failed.append(pin.__name__)
+    assert failed, f"no composed pin detects mutant {name}"
