@@ -26,9 +26,10 @@
 //   past a threshold); the four lanes that share a query row reduce with
 //   permlane swaps. With the fused prologue the raw q rows are normed and
 //   rotated in registers and the block's K rows in LDS.
-//   A unit of a split request writes its partial (O / l in fp16, max and sum
-//   in f32); a second kernel merges each request's splits in split order, so
-//   the result is deterministic.
+//   A unit of a split request writes its partial (O / l scaled by a per-row
+//   power of two into fp16, with max, sum and the scale's exponent in f32); a
+//   second kernel merges each request's splits in split order, so the result
+//   is deterministic.
 #include <algorithm>
 #include <mutex>
 
@@ -75,8 +76,8 @@ struct AttnArgs {
   const bf16* kc;
   const bf16* vc;
   bf16* out;
-  f16* part_o;        // [units * hkv][QROWS][DH]: O / l of each split (fp16)
-  float* part_ml;     // [units * hkv][QROWS][2]
+  f16* part_o;        // [units * hkv][QROWS][DH]: O / l of each split times 2^-e (fp16)
+  float* part_ml;     // [units * hkv][QROWS][4]: max, sum, e, 0
   int32_t* dir;       // [R][qtiles][hkv]: first unit index of each split set
   int64_t total_ctx, total_blk;
   int32_t* hdr;       // workspace header: [0] = keys per split chosen for this call
@@ -890,25 +891,39 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     return;
   }
 
-  // Split: publish the partial: the split's own softmax output O / l in fp16
-  // (a convex combination of V rows, so within V's range; fp16 keeps 11
-  // significant bits, 8x finer than the bf16 output) with its reference max
-  // and sum in f32. The merge kernel that follows on the stream combines the
-  // splits.
+  // Split: publish the partial: the split's own softmax output O / l (a
+  // convex combination of V rows) times 2^-e in fp16, with its reference max,
+  // sum and e in f32. e is chosen per query row so that the row's largest
+  // magnitude lands in [2^13, 2^14): fp16 then holds any finite bf16 V range
+  // without overflow and keeps 11 significant bits relative to the row's
+  // largest value (8x finer than the bf16 output), however large or small V
+  // is. The merge kernel that follows on the stream combines the splits.
   {
     const int64_t slot = (int64_t)u * a.hkv + g;
     f16* po = a.part_o + (slot * QROWS + nrow_unit) * DH + 4 * j;
     const float inv = ltot > 0.f ? 1.0f / ltot : 0.f;
+    float amax = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) amax = fmaxf(amax, fabsf(acc_o[dt][i]));
+    amax = xrow4_max(amax) * inv;
+    int ex = 0;
+    if (amax > 0.f && amax <= 3.0e38f) {
+      (void)frexpf(amax, &ex);  // amax < 2^ex
+      ex -= 14;
+    }
+    const float sc = ldexpf(inv, -ex);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) {
       f16x4 h;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) h[i] = (f16)(acc_o[dt][i] * inv);
+      for (int i = 0; i < 4; ++i) h[i] = (f16)(acc_o[dt][i] * sc);
       *reinterpret_cast<f16x4*>(po + 16 * dt) = h;
     }
     if (j == 0) {
-      float2* pml = reinterpret_cast<float2*>(a.part_ml) + slot * QROWS + nrow_unit;
-      *pml = make_float2(mx, ltot);
+      float4* pml = reinterpret_cast<float4*>(a.part_ml) + slot * QROWS + nrow_unit;
+      *pml = make_float4(mx, ltot, (float)ex, 0.f);
     }
     if (un.s == 0 && tid == 0 && a.hs.nreq == 0)
       a.dir[((int64_t)un.r * a.qtiles + un.qt) * a.hkv + g] = un.first;
@@ -966,7 +981,7 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
   }
   const int32_t nrows = a.group * blen;
   const int tid = threadIdx.x;
-  const float2* pml = reinterpret_cast<const float2*>(a.part_ml);
+  const float4* pml = reinterpret_cast<const float4*>(a.part_ml);
   constexpr int PASSES = (MROWS + RPW - 1) / RPW;
 #pragma unroll
   for (int pass = 0; pass < PASSES; ++pass) {
@@ -980,7 +995,7 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
     for (int d = 0; d < DV; ++d) o[d] = 0.f;
     float M = -INFINITY, L = 0.f;
     for (int32_t s0 = 0; s0 < ns; s0 += MB) {
-      float2 ml[MB];
+      float4 ml[MB];
       f16x8 ov[MB];
 #pragma unroll
       for (int bb = 0; bb < MB; ++bb) {
@@ -1001,10 +1016,12 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
 #pragma unroll
       for (int bb = 0; bb < MB; ++bb) {
         // split weight: its sum l times 2^(m - M); its values are O / l
+        // stored times 2^-e
         const float wgt = (s0 + bb < ns) ? ml[bb].y * fast_exp2(ml[bb].x - bsafe) : 0.f;
+        const float wov = ldexpf(wgt, (int)ml[bb].z);
         L += wgt;
 #pragma unroll
-        for (int d = 0; d < DV; ++d) o[d] += (float)ov[bb][d] * wgt;
+        for (int d = 0; d < DV; ++d) o[d] += (float)ov[bb][d] * wov;
       }
       M = bm;
     }
@@ -1296,7 +1313,7 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool p
   pl.off_part_o = off;
   off = align_up(off + sizeof(uint16_t) * (size_t)pl.units * p.num_kv_heads * QROWS * p.head_dim, 256);
   pl.off_part_ml = off;
-  off = align_up(off + sizeof(float) * 2 * (size_t)pl.units * p.num_kv_heads * QROWS, 256);
+  off = align_up(off + sizeof(float) * 4 * (size_t)pl.units * p.num_kv_heads * QROWS, 256);
   pl.bytes = (p.dtype == DFLASH_BF16) ? off : 0;
   *plan = pl;
   return true;

@@ -62,7 +62,7 @@ extern "C" {
 
 const char* dflash_last_error(void) { return g_last_error.c_str(); }
 
-int dflash_abi_version(void) { return 105; }
+int dflash_abi_version(void) { return 106; }
 
 dflash_status dflash_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
                                 void* stream) {

@@ -187,10 +187,11 @@ dflash_status dflash_block_attention_check(const dflash_block_attn_params* p);
  *   workspace  device, 256-byte aligned, >= dflash_block_attention_workspace_size
  *           bytes (no initialisation needed). It holds the partial results of
  *           key ranges that were split across work units (each split's
- *           softmax output in fp16, its max and sum in f32); one workspace
- *           must not be used by two calls that may run concurrently. Split
- *           partials are convex combinations of V rows: |V| must stay within
- *           the fp16 range (65504), far above bf16 activations in practice.
+ *           softmax output scaled per query row by a power of two into fp16,
+ *           with its max, sum and scale exponent in f32, so any finite bf16
+ *           V fits); one workspace must not be used by two calls that may run
+ *           concurrently. Products and sums accumulate in f32, which bounds
+ *           |V| by about 2^100 (far beyond any activation).
  * The result does not depend on how the keys are split into work units other
  * than through f32 rounding; for a fixed split_keys it is bitwise
  * deterministic.

@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_error_string(lib):
-    assert lib.dflash_abi_version() == 105
+    assert lib.dflash_abi_version() == 106
     assert isinstance(lib.dflash_last_error(), bytes)
 
 
