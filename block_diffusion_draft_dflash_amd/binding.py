@@ -33,6 +33,7 @@ EXPORTED = (
     "dflash_block_attention_workspace_size",
     "dflash_block_attention_check",
     "dflash_block_attention",
+    "dflash_block_attention_noalloc",
     "dflash_context_kv_workspace_size",
     "dflash_context_kv",
     "dflash_block_attention_paged",
@@ -161,6 +162,10 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.dflash_block_attention.argtypes = [ctypes.POINTER(BlockAttnParams),
                                            ctypes.POINTER(QkPrologue), P, P, P, P, P, P, P, P,
                                            P, SZ, P]
+    lib.dflash_block_attention_noalloc.restype = ctypes.c_int
+    lib.dflash_block_attention_noalloc.argtypes = [ctypes.POINTER(BlockAttnParams),
+                                                   ctypes.POINTER(QkPrologue), P, P, P, P, P, P,
+                                                   P, P, P]
     lib.dflash_context_kv_workspace_size.restype = SZ
     lib.dflash_context_kv_workspace_size.argtypes = [I64, I32, I32, I32]
     lib.dflash_context_kv.restype = ctypes.c_int
@@ -302,6 +307,24 @@ def dflash_block_attention(p: BlockAttnParams, cu_ctx_lens: torch.Tensor,
                                       _ptr(cu_ctx_lens), _ptr(cu_blk_lens),
                                       _ptr(q), _ptr(k_blk), _ptr(v_blk), _ptr(k_ctx), _ptr(v_ctx),
                                       _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20  # DFLASH_NOALLOC_SCRATCH_BYTES
+
+
+def dflash_block_attention_noalloc(p: BlockAttnParams, cu_ctx_lens: torch.Tensor,
+                                   cu_blk_lens: torch.Tensor, q: torch.Tensor, k_blk: torch.Tensor,
+                                   v_blk: torch.Tensor, k_ctx: Optional[torch.Tensor],
+                                   v_ctx: Optional[torch.Tensor], out: torch.Tensor, stream=None,
+                                   prologue: Optional[QkPrologue] = None) -> None:
+    """``dflash_block_attention`` with the library's own per-GPU scratch in
+    place of a caller workspace (for callers that cannot allocate)."""
+    lib = load()
+    _check(lib.dflash_block_attention_noalloc(ctypes.byref(p),
+                                              ctypes.byref(prologue) if prologue is not None else None,
+                                              _ptr(cu_ctx_lens), _ptr(cu_blk_lens), _ptr(q),
+                                              _ptr(k_blk), _ptr(v_blk), _ptr(k_ctx), _ptr(v_ctx),
+                                              _ptr(out), _stream(stream)))
 
 
 def dflash_context_kv_workspace_size(T: int, hidden_size: int, num_kv_heads: int,

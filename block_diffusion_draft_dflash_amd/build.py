@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
 SOURCES = ["dflash_api.hip", "rope_qknorm.hip", "block_attention.hip", "context_kv.hip",
-           "kv_store.hip", "layer_proj.hip", "propose_prep.hip"]
+           "kv_store.hip", "layer_proj.hip", "propose_prep.hip", "noalloc_scratch.hip"]
 ARCH = "gfx950"
 
 # Packed-FP32 instructions are disabled for every HIP translation unit.

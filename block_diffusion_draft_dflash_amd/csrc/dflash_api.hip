@@ -255,6 +255,32 @@ dflash_status dflash_block_attention(const dflash_block_attn_params* p,
                               k_blk, v_blk, k_ctx, v_ctx, out, workspace, workspace_bytes, stream);
 }
 
+dflash_status dflash_block_attention_noalloc(const dflash_block_attn_params* p,
+                                             const dflash_qk_prologue* prologue,
+                                             const int32_t* cu_ctx_lens,
+                                             const int32_t* cu_blk_lens, const void* q,
+                                             const void* k_blk, const void* v_blk,
+                                             const void* k_ctx, const void* v_ctx, void* out,
+                                             void* stream) {
+  dflash_status st = dflash_block_attention_check(p);
+  if (st != DFLASH_OK) return st;
+  dflash::AttnPlan plan;
+  dflash::plan_block_attention(*p, kPlanComputeUnits, false, &plan);
+  if (plan.bytes > DFLASH_NOALLOC_SCRATCH_BYTES)
+    return fail(DFLASH_ERR_WORKSPACE,
+                "block_attention_noalloc: this batch needs %zu bytes of scratch, more than the "
+                "%zu the library holds per GPU (call dflash_block_attention with a workspace)",
+                plan.bytes, (size_t)DFLASH_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (plan.bytes > 0 && p->total_blk > 0) {
+    const hipError_t e = dflash::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, "block_attention_noalloc: scratch address");
+  }
+  return block_attention_impl("block_attention_noalloc", p, nullptr, prologue, cu_ctx_lens,
+                              cu_blk_lens, q, k_blk, v_blk, k_ctx, v_ctx, out, ws,
+                              DFLASH_NOALLOC_SCRATCH_BYTES, stream);
+}
+
 dflash_status dflash_block_attention_paged(const dflash_block_attn_params* p,
                                            const dflash_paged_ctx* pg,
                                            const dflash_qk_prologue* prologue,

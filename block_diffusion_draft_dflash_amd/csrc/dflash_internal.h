@@ -66,6 +66,11 @@ size_t fc_combine_workspace_bytes(int64_t T, int32_t hidden, int32_t taps, int n
 hipError_t launch_fc_combine(const float* aux, const void* w_fc, int64_t T, int32_t hidden,
                              int32_t taps, void* out, void* ws, int num_cus, hipStream_t s);
 
+// Device address of the current device's copy of the allocation-free entry
+// point's scratch array (DFLASH_NOALLOC_SCRATCH_BYTES bytes), looked up on the
+// first call on each device.
+hipError_t noalloc_scratch(void** addr);
+
 hipError_t launch_prepare_inputs(const dflash_prepare_params& p, const dflash_prepare_inputs_in& in,
                                  const dflash_prepare_inputs_out& out, hipStream_t s);
 

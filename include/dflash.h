@@ -205,6 +205,34 @@ dflash_status dflash_block_attention(const dflash_block_attn_params* p,
                                      void* stream);
 
 /*
+ * dflash_block_attention_noalloc -- dflash_block_attention for callers that
+ * cannot allocate device memory (code under HIP-graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same computation, arguments
+ * and result (bitwise, for the same parameters) with the workspace taken from
+ * a scratch array the library holds on each GPU instead of a caller buffer.
+ *
+ * The scratch is DFLASH_NOALLOC_SCRATCH_BYTES (32 MiB) per GPU, held until
+ * the process ends; it covers every batch whose
+ * dflash_block_attention_workspace_size is at most that (e.g. 64 requests of
+ * up to 8192 context rows with 16-row blocks, Hq 32, Hkv 8, Dh 128: 17 MiB).
+ * Larger workspaces are rejected with DFLASH_ERR_WORKSPACE before anything is
+ * enqueued. Nothing in the scratch needs to start at zero (every partial is
+ * written before it is read within a call). All calls on one GPU share that
+ * GPU's scratch: calls that may overlap on one GPU (on different streams, or
+ * from different threads without ordering) race and must not be issued. The
+ * first call on a device looks up the scratch's device address (a host-side
+ * query, not a stream operation); the call itself allocates nothing.
+ */
+#define DFLASH_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+dflash_status dflash_block_attention_noalloc(const dflash_block_attn_params* p,
+                                             const dflash_qk_prologue* prologue,
+                                             const int32_t* cu_ctx_lens,
+                                             const int32_t* cu_blk_lens, const void* q,
+                                             const void* k_blk, const void* v_blk,
+                                             const void* k_ctx, const void* v_ctx, void* out,
+                                             void* stream);
+
+/*
  * Paged context store ("qwen3_dflash.cpp" page, the fixed-capacity paged
  * draft-KV store read by the paged block attention in ForwardPagedBody): a
  * pool [num_pages, page_size, Hkv, Dh] per tensor (K and V), and per request

@@ -275,3 +275,23 @@ def test_fc_combine_validation(lib):
     assert f(fake, fake, 4, 4096, 0, fake, fake, 1 << 30, None) == B.DFLASH_ERR_INVALID_ARG
     assert f(fake, fake, 4, 4096, 5, fake, None, 0, None) == B.DFLASH_ERR_WORKSPACE
     assert B.dflash_fc_combine_workspace_size(128, 4096, 5) >= 128 * 4096 * 5 * 2
+
+
+def test_noalloc_rejects_before_touching_the_gpu(lib):
+    # host-side checks of the allocation-free entry point return before any
+    # HIP call: invalid parameters, a batch whose workspace exceeds the
+    # library's per-GPU scratch, and an empty batch (nothing to do)
+    f = lambda p: lib.dflash_block_attention_noalloc(ctypes.byref(p), None, None, None, None, None,
+                                                     None, None, None, None, None)
+    assert f(P(num_reqs=0)) == B.DFLASH_ERR_INVALID_ARG
+    big = P(total_ctx=1 << 24, split_keys=64)
+    assert B.dflash_block_attention_workspace_size(big) > B.NOALLOC_SCRATCH_BYTES
+    assert f(big) == B.DFLASH_ERR_WORKSPACE
+    assert "scratch" in lib.dflash_last_error().decode()
+    assert f(P(total_blk=0, max_blk_len=0)) == B.DFLASH_OK
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define DFLASH_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
