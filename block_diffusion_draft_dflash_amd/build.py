@@ -26,10 +26,13 @@ ARCH = "gfx950"
 HIPFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-result",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-    # keep MFMA accumulators in VGPRs (the softmax rescale touches them)
-    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Keep MFMA accumulators in VGPRs (the attention's softmax rescale and the
+# projections' epilogues touch them); the context GEMM's 256 accumulators per
+# lane live in the accumulation registers instead.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form"]
+AGPR_ACC_SOURCES = {"context_kv.hip"}
 
 
 def _hipcc() -> str:
@@ -41,7 +44,8 @@ def _hipcc() -> str:
 
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [_hipcc(), *HIPFLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    extra = [] if src in AGPR_ACC_SOURCES else VGPR_FORM
+    cmd = [_hipcc(), *HIPFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -11,15 +11,15 @@
 // so the weights are pre-multiplied by hidden_norm once per call (rounded to
 // bf16, the reference rounds the normed activations instead) and 1/rms_t is
 // applied in the GEMM epilogue; the GEMM computes it from the A fragments
-// its waves already hold (no separate pass over the hidden states). The GEMM (M = rows, N = 2 * Hkv * Dh, K = H)
-// runs on v_mfma_f32_16x16x32_bf16 with 256x256 workgroup tiles of 8 waves
-// (two per SIMD); a wave owns 128 rows x 64 columns of one 128-wide head,
-// chosen so that the rotate-half pairs (d, d + 64) meet in one lane; the
-// k-norm's sum of squares is completed with the partner wave through LDS.
-// The k-slices of A and B are copied HBM -> LDS directly (no register
-// staging) up to NSTAGE slices ahead, with explicit waits and fence-free
-// barriers, and each wave reads the next slice's fragments while the MFMAs
-// of the current one run.
+// its waves already hold (no separate pass over the hidden states). The GEMM
+// (M = rows, N = 2 * Hkv * Dh, K = H) runs on v_mfma_f32_16x16x32_bf16 with
+// 256x256 workgroup tiles of 4 waves (one per SIMD); a wave owns 128 rows x
+// one whole 128-wide head, so the k-norm and the rotate-half pairs (d, d + 64)
+// stay inside the wave. The k-slices of A and B are copied HBM -> LDS
+// directly (no register staging) up to NSTAGE - 1 slices ahead, with explicit
+// waits and fence-free barriers, and each wave reads the next slice's
+// fragments while the MFMAs of the current one run. The epilogue stages each
+// wave's bf16 tile in LDS and writes whole 16-byte pieces of the output rows.
 #include <mutex>
 
 #include "dflash_device.h"
@@ -28,7 +28,7 @@
 namespace dflash {
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32;
+constexpr int BM = 256, BN = 256, BK = 64;
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -66,16 +66,17 @@ struct CkvArgs {
   float eps;
 };
 
-// A and B tiles are [256 rows][32 k] bf16 (64-byte rows, 4 chunks of 16 B);
-// chunk c of row r is stored at c ^ ((r >> 1) & 3). A fragment read (16
-// consecutive rows at one logical chunk) is served 8 lanes = 128 bytes at a
-// time; rows 2i and 2i + 1 share a 128-byte line at offsets 0 and 64, and the
-// XOR moves each pair of the 8 rows to its own 16-byte slot, so the 8 lanes hit
-// distinct banks. (The former c ^ ((r >> 2) & 3) put rows r and r + 2 in the
-// same banks: 48% of the GEMM's LDS cycles were bank conflicts.)
-__device__ __forceinline__ int tswz(int row, int c) { return c ^ ((row >> 1) & 3); }
+// A and B k-stages are [256 rows][64 k] bf16 (128-byte rows, 8 chunks of
+// 16 B); chunk c of row r is stored at c ^ ((r >> 1) & 7). A 32x32x16
+// fragment read takes 32 consecutive rows at logical chunk c (lanes 0-31) and
+// c + 1 (lanes 32-63); with this swizzle the read has no bank conflicts
+// (measured with the LDS bank-conflict counter).
+__device__ __forceinline__ int tswz(int row, int c) { return c ^ ((row >> 1) & 7); }
 
-constexpr int NSTAGE = 4;  // LDS stages of (A, B) k-slices: NSTAGE - 1 in flight
+#ifndef SCHED_CORE
+#define SCHED_CORE 1
+#endif
+constexpr int NSTAGE = 2;  // LDS stages of 64-k (A, B) slices: the next one in flight
 
 // s_waitcnt on the vector-memory counter only (gfx9 encoding: vmcnt in bits
 // 3:0 and 15:14; expcnt and lgkmcnt left at their no-wait maxima).
@@ -84,6 +85,7 @@ __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 // Workgroup barrier without the memory fence of __syncthreads() (which would
 // drain the k-slices still in flight).
 __device__ __forceinline__ void block_barrier() {
@@ -92,20 +94,49 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-constexpr int NTG = 512;  // GEMM workgroup: 8 waves, two per SIMD
+constexpr int NTG = 256;  // GEMM workgroup: 4 waves, one per SIMD
 
-__global__ __launch_bounds__(NTG) void ctx_kv_gemm_kernel(CkvArgs a) {
+// Sum over the 32 lanes of each half of the wave with DPP swaps (quad xor 1,
+// quad xor 2, half-row and row mirrors) and one 16-lane row swap.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float lane32_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  const int x = __float_as_int(v);
+  auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return __int_as_float(b[0]) + __int_as_float(b[1]);
+}
+
+// One workgroup computes a 256-row x 256-column tile (two heads) of
+// [K | V] = h W'^T over the whole of H. Wave w owns rows 128 (w & 1) ..+127
+// and head (w >> 1) of the tile: 4 x 4 blocks of 32 x 32 outputs on
+// v_mfma_f32_32x32x16_bf16, whose 256 f32 accumulators per lane sit in the
+// accumulation registers. (With one wave per SIMD the 32x32 form keeps the
+// matrix pipe busy back to back; measured on this GPU, the 16x16x32 form
+// reaches ~1.4 PFLOP/s from one wave per SIMD against ~2.2 for 32x32x16.)
+// Each 64-k stage is consumed as two 32-k sub-slices: per sub-slice a wave
+// reads 8 A and 8 B fragments from LDS (16 KB) for 32 MFMAs, the next
+// sub-slice's fragments being read, and the current A fragments' squares
+// summed for the row norm, in between those MFMAs. One barrier per stage.
+// The body is instantiated per head of the tile (WN, the waves' w >> 1) so
+// that each wave's share of the row-norm sums (k-half WN of every sub-slice)
+// selects its fragments at compile time.
+template <int WN>
+__device__ __forceinline__ void ctx_kv_gemm_body(const CkvArgs& a, bf16* smem) {
   constexpr int DH = 128;
   constexpr int HALF = DH / 2;
-  constexpr int TILE = BM * BK;               // elements per A (or B) k-slice
+  constexpr int TILE = BM * BK;               // elements per A (or B) stage
   constexpr int NW = NTG / 64;
-  constexpr int CPW = TILE / 512 / NW;        // 1 KB copies per wave per operand per k-slice (2)
-  constexpr int CPS = 2 * CPW;                // per thread per k-slice (A and B)
-  extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][A | B]
+  constexpr int CPW = TILE / 512 / NW;        // 1 KB copies per wave per operand per stage (8)
 
   // Block order: the dispatcher deals workgroups to the 8 XCDs round-robin.
   // Consecutive row blocks go to different XCDs and each XCD runs all column
-  // tiles of its row blocks.
+  // tiles of its row blocks together (they read the same A slices).
   const int ntn = a.n / BN;
   const int xcd = blockIdx.x % 8;
   const int slot = blockIdx.x / 8;
@@ -114,211 +145,293 @@ __global__ __launch_bounds__(NTG) void ctx_kv_gemm_kernel(CkvArgs a) {
   if (row0 >= a.rows) return;
   const int col0 = (slot % ntn) * BN;
   const int tid = threadIdx.x;
-  const int w = tid >> 6, lane = tid & 63, m = lane & 15, j = lane >> 4;
-  // Wave tile: 128 rows (half wm) x 64 columns of head hw of the tile: the
-  // 32-column chunks cc and cc + 2 of the head (columns d and d + 64 of a
-  // rotate-half pair are in the same lane); the partner wave (w ^ 2) holds
-  // the head's other 64 columns.
-  const int wm = w & 1, wn = w >> 1, hw = wn >> 1, cc = wn & 1;
-  auto hcol = [&](int y) { return (y >> 1) * HALF + cc * 32 + (y & 1) * 16; };  // column in head
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int l32 = lane & 31, hi = lane >> 5;  // MFMA row / column within a block, lane half
+  const int wm = w & 1;
+  constexpr int wn = WN;
 
-  const bf16* asrc[CPW];
-  const bf16* bsrc[CPW];
+  // Copy sources: a scalar base per operand (the workgroup's first row, then
+  // advanced one stage per copy) and a 32-bit byte offset per lane and copy:
+  // a 1 KB copy fills 8 rows of 128 bytes, lane l row l / 8 at logical chunk
+  // tswz(row, l % 8).
+  const bf16* abase = a.h + row0 * a.hidden;
+  const bf16* bbase = a.w + (int64_t)col0 * a.hidden;
+  // (B has no partial tiles: its offset is a lane part, which depends on the
+  // copy's parity only, plus a uniform part folded into the base)
+  uint32_t aoff[CPW], boff[2];
 #pragma unroll
   for (int i = 0; i < CPW; ++i) {
-    const int r = (w * CPW + i) * 16 + lane / 4;
-    const int c = tswz(r, lane % 4);
-    const int64_t grow = min(row0 + r, a.rows - 1);
-    asrc[i] = a.h + grow * a.hidden + c * 8;
-    bsrc[i] = a.w + (int64_t)(col0 + r) * a.hidden + c * 8;
+    const int r = (w * CPW + i) * 8 + lane / 8;
+    const int c = tswz(r, lane % 8);
+    const int ra = (int)min((int64_t)r, a.rows - 1 - row0);  // rows past the end re-read the last
+    aoff[i] = (uint32_t)(ra * a.hidden + c * 8) * 2u;
+    if (i < 2) boff[i] = (uint32_t)(r * a.hidden + c * 8) * 2u;
   }
-  auto dma = [](const bf16* src, bf16* dst) {
-    const uint32_t lds_addr =
-        __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)dst);
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+  // LDS byte address of the dynamic shared memory (uniform)
+  const uint32_t lds0 = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(DF_LDS void*)smem);
+  auto dma = [](const bf16* base, uint32_t voff, uint32_t lds_addr) {
+    // the base is uniform; say so, so that it sits in scalar registers
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, %2"
                  :
-                 : "s"(lds_addr), "v"(src)
+                 : "s"(lds_addr), "v"(voff), "s"(sb)
                  : "memory", "m0");
   };
-  auto issue = [&](int32_t ks) {
-    bf16* as = smem + (ks % NSTAGE) * 2 * TILE;
-    bf16* bs = as + TILE;
-    const int32_t k0 = ks * BK;
+  constexpr uint32_t STAGE_BYTES = 2 * TILE * sizeof(bf16);
+  auto issue = [&](int32_t st_idx) {
+    const uint32_t st = lds0 + (uint32_t)(st_idx % NSTAGE) * STAGE_BYTES;
+    const int32_t k0 = st_idx * BK;
 #pragma unroll
     for (int i = 0; i < CPW; ++i) {
-      dma(asrc[i] + k0, as + (w * CPW + i) * 512);
-      dma(bsrc[i] + k0, bs + (w * CPW + i) * 512);
+      dma(abase + k0, aoff[i], st + (w * CPW + i) * 1024);
+      dma(bbase + k0 + (int64_t)(i & ~1) * 8 * a.hidden, boff[i & 1], st + TILE * 2 + (w * CPW + i) * 1024);
     }
   };
 
-  f32x4 acc[8][4];
+  f32x16 acc[4][4];
 #pragma unroll
-  for (int x = 0; x < 8; ++x)
+  for (int x = 0; x < 4; ++x)
 #pragma unroll
-    for (int y = 0; y < 4; ++y) acc[x][y] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[x][y][e] = 0.f;
 
-  auto read_frags = [&](int32_t ks, bf16x8 (&af)[8], bf16x8 (&bfr)[4]) {
-    const bf16* as = smem + (ks % NSTAGE) * 2 * TILE;
-    const bf16* bs = as + TILE;
+  // Fragment (x, h) of sub-slice j of A: rows 128 wm + 32 x + l32, k 32 j +
+  // 16 h + 8 hi .. +7 of the stage (logical chunk 4 j + 2 h + hi); B likewise
+  // over rows 128 wn + 32 y + l32. The swizzle depends on l32 only, so each
+  // (operand, j, h) has one per-lane base and the blocks sit at fixed offsets.
+  int a_lane[2][2], b_lane[2][2];
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int ra = 128 * wm + 16 * x + m;
-      af[x] = *reinterpret_cast<const bf16x8*>(as + ra * BK + tswz(ra, j) * 8);
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      a_lane[jj][h] = (128 * wm + l32) * BK + tswz(l32, 4 * jj + 2 * h + hi) * 8;
+      b_lane[jj][h] = TILE + (128 * wn + l32) * BK + tswz(l32, 4 * jj + 2 * h + hi) * 8;
     }
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int rbb = hw * DH + hcol(y) + m;
-      bfr[y] = *reinterpret_cast<const bf16x8*>(bs + rbb * BK + tswz(rbb, j) * 8);
-    }
+  auto frag = [&](int32_t st_idx, int lane_off, int x) {
+    const bf16* p = smem + (st_idx % NSTAGE) * 2 * TILE + lane_off;
+    return *reinterpret_cast<const bf16x8*>(p + x * 32 * BK);
   };
-  auto mma = [&](const bf16x8 (&af)[8], const bf16x8 (&bfr)[4]) {
-#pragma unroll
-    for (int x = 0; x < 8; ++x)
-#pragma unroll
-      for (int y = 0; y < 4; ++y)
-        acc[x][y] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[x], bfr[y], acc[x][y], 0, 0, 0);
-  };
-  // wait until this thread's copies of slice t landed, given the last slice issued
-  auto wait_slice = [&](int32_t t, int32_t last) {
-    const int32_t after = min(last - t, NSTAGE - 1);
-    if (after >= 3) wait_vmcnt<3 * CPS>();
-    else if (after == 2) wait_vmcnt<2 * CPS>();
-    else if (after == 1) wait_vmcnt<CPS>();
-    else wait_vmcnt<0>();
-  };
-  auto lgkm0 = [] { __builtin_amdgcn_s_waitcnt(0xC07F); };
+  const int32_t nst = a.hidden / BK;  // stages (H is a multiple of 64)
 
-  const int32_t ksteps = a.hidden / BK;
-  auto read_a = [&](int32_t ks, bf16x8 (&af)[8]) {
-    const bf16* as = smem + (ks % NSTAGE) * 2 * TILE;
+  // hidden row sums of squares of rows 128 wm + 32 x + l32, this wave's share:
+  // k-half WN of every sub-slice (the other head's wave takes the other half),
+  // one bf16 dot product per pair of elements, into two independent partial
+  // sums per row so that no dot product waits for the previous one
+  float hsq[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  auto row_sum_part = [&](const bf16x8& v8, int x, int half) {
 #pragma unroll
-    for (int x = 0; x < 8; ++x) {
-      const int ra = 128 * wm + 16 * x + m;
-      af[x] = *reinterpret_cast<const bf16x8*>(as + ra * BK + tswz(ra, j) * 8);
+    for (int e = 2 * half; e < 2 * half + 2; ++e) {
+      const bf16x2 p2 = {v8[2 * e], v8[2 * e + 1]};
+      hsq[x][e & 1] = __builtin_amdgcn_fdot2_f32_bf16(p2, p2, hsq[x][e & 1], false);
     }
   };
-  auto read_b = [&](int32_t ks, bf16x8 (&bfr)[4]) {
-    const bf16* bs = smem + (ks % NSTAGE) * 2 * TILE + TILE;
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int rbb = hw * DH + hcol(y) + m;
-      bfr[y] = *reinterpret_cast<const bf16x8*>(bs + rbb * BK + tswz(rbb, j) * 8);
-    }
+  // fragments of one sub-slice: [0..3] B blocks at k-half 0, [4..7] at k-half
+  // 1 (read first, every MFMA needs them), then A likewise
+  auto read_frag = [&](int32_t st_idx, int jj, int q, bf16x8 (&na)[8], bf16x8 (&nb)[8]) {
+    if (q < 8) nb[q] = frag(st_idx, b_lane[jj][q >> 2], q & 3);
+    else na[q - 8] = frag(st_idx, a_lane[jj][(q - 8) >> 2], (q - 8) & 3);
   };
-  int32_t last = -1;
+  auto mma = [&](const bf16x8 (&ca)[8], const bf16x8 (&cb)[8], int x, int h, int y) {
+    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[4 * h + x], cb[4 * h + y], acc[x][y],
+                                                        0, 0, 0);
+  };
+  // The 32 MFMAs of one sub-slice on (ca, cb), with the 16 fragment reads of
+  // the next sub-slice (stage st_idx, half jj) into (na, nb) between them.
+  auto core = [&](const bf16x8 (&ca)[8], const bf16x8 (&cb)[8], bf16x8 (&na)[8],
+                  bf16x8 (&nb)[8], int32_t st_idx, int jj) {
 #pragma unroll
-  for (int t = 0; t < NSTAGE; ++t)
-    if (t < ksteps) { issue(t); last = t; }
-  bf16x8 fa[8], fb[4], gb[4];
-  float hsq[2] = {0.f, 0.f};  // hidden row sums of squares, row blocks 2wn and 2wn + 1
-  wait_slice(0, last);
-  block_barrier();
-  read_b(0, fb);
-  for (int32_t ks = 0; ks < ksteps; ++ks) {
-    read_a(ks, fa);
-    // B of slice ks in fb; A of slice ks read above; B of ks+1 under the MFMAs
-    if (ks + 1 < ksteps) {
-      wait_slice(ks + 1, last);
-      lgkm0();
-      block_barrier();
-      if (ks + NSTAGE < ksteps) { issue(ks + NSTAGE); last = ks + NSTAGE; }
-      read_b(ks + 1, gb);
+    for (int q = 0; q < 16; ++q) {
+      const int x = q >> 2, h = (q >> 1) & 1, y0 = 2 * (q & 1);
+      read_frag(st_idx, jj, q, na, nb);
+      mma(ca, cb, x, h, y0);
+      mma(ca, cb, x, h, y0 + 1);
     }
-    mma(fa, fb);
-    // the four waves that share these A rows split the row sums: wave wn takes
-    // row blocks 2wn, 2wn + 1 (selected without dynamic register indexing)
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
-      if ((x >> 1) == wn) {
+    for (int x = 0; x < 4; ++x) {
+      row_sum_part(ca[4 * WN + x], x, 0);
+      row_sum_part(ca[4 * WN + x], x, 1);
+    }
+#if SCHED_CORE
+    // one fragment read per two MFMAs: at most a few LDS reads outstanding at
+    // any time (the LDS counter holds 15), none of them holding up an MFMA
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = bf2f(fa[x][e]);
-          hsq[x & 1] += v * v;
+    for (int q = 0; q < 16; ++q) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // 1 LDS read
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 1, 0);  // 1 VALU
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+    }
+#endif
+  };
+  auto core_last = [&](const bf16x8 (&ca)[8], const bf16x8 (&cb)[8]) {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int y = 0; y < 4; ++y) mma(ca, cb, x, h, y);
+        if (h == WN) {
+          row_sum_part(ca[4 * h + x], x, 0);
+          row_sum_part(ca[4 * h + x], x, 1);
         }
       }
-#pragma unroll
-    for (int y = 0; y < 4; ++y) fb[y] = gb[y];
-  }
+  };
 
-  // Row scale of the hidden RMSNorm, from the A fragments the waves consumed:
-  // 1 / sqrt(mean(h^2) + eps) per row, shared through LDS.
-  float* rst = reinterpret_cast<float*>(smem) + NW * 128;  // [256]
-  lgkm0();
+  bf16x8 fa[8], fb[8], ga[8], gb[8];
+  issue(0);
+  if (nst > 1) {
+    issue(1);
+    wait_vmcnt<2 * CPW>();  // stage 0 landed (stage 1 may stay in flight)
+  } else {
+    wait_vmcnt<0>();
+  }
+  block_barrier();
+#pragma unroll
+  for (int q = 0; q < 16; ++q) read_frag(0, 0, q, fa, fb);
+  for (int32_t st = 0; st + 1 < nst; ++st) {
+    // first half of stage st, while its second half's fragments are read
+    core(fa, fb, ga, gb, st, 1);
+    // stage st + 1 landed everywhere, and every wave's reads of stage st are
+    // done: stage st's buffer takes stage st + 2
+    wait_vmcnt<0>();
+    wait_lgkm0();
+    block_barrier();
+    if (st + 2 < nst) issue(st + 2);
+    core(ga, gb, fa, fb, st + 1, 0);
+  }
+  core(fa, fb, ga, gb, nst - 1, 1);  // the last stage
+  core_last(ga, gb);
+
+  // Row scale of the hidden RMSNorm, 1 / sqrt(mean(h^2) + eps): the two
+  // waves' partial sums of each row meet in LDS (after the transposition area
+  // of the epilogue), with the rows' positions (K tiles).
+  float* rpart = reinterpret_cast<float*>(smem + NW * 128 * 128);  // [2][256]
+  float* rsc = rpart + 512;                                       // [256] row scales
+  int32_t* rpos = reinterpret_cast<int32_t*>(rsc + 256);          // [256] clamped positions
+  const int head = (col0 + DH * wn) / DH;  // 0..2*Hkv-1: K heads first, then V heads
+  const bool is_k = col0 < a.hkv * DH;     // a 256-column tile is all K or all V
+  int32_t my_pos = 0;
+  if (is_k) my_pos = a.pos[min(row0 + tid, a.rows - 1)];
+  wait_lgkm0();
   block_barrier();  // every wave is done with the stages
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const float ss = xrow4_sum(hsq[h]);  // the 4 lane groups cover the row's k chunks
-    if (j == 0) rst[128 * wm + 16 * (2 * wn + h) + m] = 1.0f / sqrtf(ss / (float)a.hidden + a.eps);
+  for (int x = 0; x < 4; ++x) {
+    const float ss = hsq[x][0] + hsq[x][1];
+    const float s2 = ss + __shfl_xor(ss, 32, 64);  // both lane halves' k chunks
+    if (hi == 0) rpart[256 * WN + 128 * wm + 32 * x + l32] = s2;
   }
-  lgkm0();
+  rpos[tid] = my_pos < 0 ? 0 : (my_pos >= a.max_pos ? a.max_pos - 1 : my_pos);
+  wait_lgkm0();
   block_barrier();
-  // Epilogue. acc[x][y][i] = C[row0 + 128 wm + 16x + 4j + i][col0 + 128 hw + hcol(y) + m].
-  const int head = (col0 + DH * hw) / DH;  // 0..2*Hkv-1: K heads first, then V heads
-  const bool is_k = col0 < a.hkv * DH;     // a 256-column tile is all K or all V
+  rsc[tid] = 1.0f / sqrtf((rpart[tid] + rpart[256 + tid]) / (float)a.hidden + a.eps);
+  wait_lgkm0();
+  block_barrier();
+
+  // Epilogue. acc[x][y][e] = C[row0 + 128 wm + 32 x + 8 (e / 4) + 4 hi + e % 4]
+  //                           [col0 + 128 wn + 32 y + l32]:
+  // this wave holds one whole head of its 128 rows, so the k-norm's sums and
+  // the rotate-half pairs (d, d + 64) = blocks (y, y + 2) stay in the wave.
   bf16* dst_base = is_k ? a.k_out : a.v_out;
   const int hh = is_k ? head : head - a.hkv;
+  // The wave's bf16 tile goes through LDS ([128 rows][128 cols], 16-byte
+  // chunk q of row r at q ^ (r & 15)) so that the stores are whole 16-byte
+  // pieces of each 256-byte output row.
+  bf16* tl = smem + w * 128 * 128;
+  auto rloc_of = [&](int x, int e) { return 32 * x + 8 * (e >> 2) + 4 * hi + (e & 3); };
+  auto store_lds = [&](int rloc, const float (&v)[4]) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y) {
+      const int col = 32 * y + l32;
+      tl[rloc * 128 + (((col >> 3) ^ (rloc & 15)) << 3) + (col & 7)] = f2bf(v[y]);
+    }
+  };
   if (is_k) {
-    // per-head RMSNorm: this wave's 64 columns of each row, then the partner's
-    float* sq = reinterpret_cast<float*>(smem);  // [NW][128]
+    float kw[4];
 #pragma unroll
-    for (int x = 0; x < 8; ++x)
+    for (int y = 0; y < 4; ++y) kw[y] = a.knw[32 * y + l32];
+    // cos/sin of the lane's pairs (d = 32 y + l32, y < 2) for 8 rows at a
+    // time (half of block x), fetched one group ahead
+    float2 cs[2][8][2];
+    auto fetch = [&](int g, float2 (&c)[8][2]) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t row = row0 + 128 * wm + 16 * x + 4 * j + i;
-        const float rs = row < a.rows ? rst[128 * wm + 16 * x + 4 * j + i] : 0.f;
+      for (int i = 0; i < 8; ++i) {
+        const int e = 8 * (g & 1) + i;
+        const float2* t = a.table + (int64_t)rpos[128 * wm + rloc_of(g >> 1, e)] * HALF + l32;
+        c[i][0] = t[0];
+        c[i][1] = t[32];
+      }
+    };
+    fetch(0, cs[0]);
+#pragma unroll
+    for (int g = 0; g < 8; ++g) {
+      if (g + 1 < 8) fetch(g + 1, cs[(g + 1) & 1]);
+      const int x = g >> 1;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int e = 8 * (g & 1) + i;
+        const int rloc = rloc_of(x, e);
+        const float rs = rsc[128 * wm + rloc];
+        float v[4];
         float ss = 0.f;
 #pragma unroll
         for (int y = 0; y < 4; ++y) {
-          const float v = acc[x][y][i] * rs;
-          ss += v * v;
+          v[y] = acc[x][y][e] * rs;
+          ss += v[y] * v[y];
         }
-        ss = group_sum<16>(ss);  // the 16 lanes of group j hold this row's 64 columns
-        if (m == 0) sq[w * 128 + 16 * x + 4 * j + i] = ss;
-      }
-    lgkm0();
-    block_barrier();
-  }
-  float kw[4];
-#pragma unroll
-  for (int y = 0; y < 4; ++y) kw[y] = a.knw[hcol(y) + m];
-#pragma unroll
-  for (int x = 0; x < 8; ++x) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int rloc = 16 * x + 4 * j + i;
-      const int64_t row = row0 + 128 * wm + rloc;
-      const bool rv = row < a.rows;
-      const float rs = rv ? rst[rloc + 128 * wm] : 0.f;
-      float y4[4];
-#pragma unroll
-      for (int y = 0; y < 4; ++y) y4[y] = acc[x][y][i] * rs;
-      if (is_k) {
-        const float* sq = reinterpret_cast<const float*>(smem);
-        const float ss = sq[w * 128 + rloc] + sq[(w ^ 2) * 128 + rloc];
+        ss = lane32_sum(ss);  // the 32 lanes of this half hold the row's 128 columns
         const float inv = 1.0f / sqrtf(ss * (1.0f / DH) + a.eps);
 #pragma unroll
-        for (int y = 0; y < 4; ++y) y4[y] *= inv * kw[y];
-        if (rv) {
-          int32_t p = a.pos[row];
-          p = p < 0 ? 0 : (p >= a.max_pos ? a.max_pos - 1 : p);
-          const float2* cs = a.table + (int64_t)p * HALF;
-#pragma unroll
-          for (int y = 0; y < 2; ++y) {  // pairs (d, d + 64): y and y + 2
-            const float2 c = cs[hcol(y) + m];
-            const float lo = y4[y], hi = y4[y + 2];
-            y4[y] = lo * c.x - hi * c.y;
-            y4[y + 2] = hi * c.x + lo * c.y;
-          }
+        for (int y = 0; y < 2; ++y) {  // pairs (d, d + 64): blocks y and y + 2
+          const float2 c = cs[g & 1][i][y];
+          const float lo = v[y] * inv * kw[y], hi2 = v[y + 2] * inv * kw[y + 2];
+          v[y] = lo * c.x - hi2 * c.y;
+          v[y + 2] = hi2 * c.x + lo * c.y;
         }
-      }
-      if (rv) {
-        bf16* dst = dst_base + (row * a.hkv + hh) * DH + m;
-#pragma unroll
-        for (int y = 0; y < 4; ++y) dst[hcol(y)] = f2bf(y4[y]);
+        store_lds(rloc, v);
       }
     }
+  } else {
+#pragma unroll
+    for (int x = 0; x < 4; ++x)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int rloc = rloc_of(x, e);
+        const float rs = rsc[128 * wm + rloc];
+        float v[4];
+#pragma unroll
+        for (int y = 0; y < 4; ++y) v[y] = acc[x][y][e] * rs;
+        store_lds(rloc, v);
+      }
+  }
+  wait_lgkm0();  // the wave reads back only its own tile
+#pragma unroll 4
+  for (int it = 0; it < 32; ++it) {
+    const int rloc = it * 4 + (lane >> 4);
+    const int q = lane & 15;
+    const int64_t row = row0 + 128 * wm + rloc;
+    const bf16x8 v = *reinterpret_cast<const bf16x8*>(tl + rloc * 128 + ((q ^ (rloc & 15)) << 3));
+    if (row < a.rows)
+      *reinterpret_cast<bf16x8*>(dst_base + (row * a.hkv + hh) * DH + q * 8) = v;
   }
 }
+
+__global__ __launch_bounds__(NTG) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void ctx_kv_gemm_kernel(CkvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) bf16 smem[];  // [stage][A | B]
+  if (__builtin_amdgcn_readfirstlane(threadIdx.x >> 7) == 0) ctx_kv_gemm_body<0>(a, smem);
+  else ctx_kv_gemm_body<1>(a, smem);
+}
+
+// LDS of the GEMM: the k-slice stages, or in the epilogue the four waves'
+// 128 x 128 bf16 tiles, the partial row sums, row scales and positions,
+// whichever is larger.
+constexpr size_t kGemmLds = (size_t)NSTAGE * 2 * BM * BK * sizeof(bf16) > (size_t)4 * 128 * 128 * 2 + 4096
+                                ? (size_t)NSTAGE * 2 * BM * BK * sizeof(bf16)
+                                : (size_t)4 * 128 * 128 * 2 + 4096;
 
 }  // namespace
 
@@ -356,14 +469,14 @@ hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* w
   a.eps = eps;
   const int64_t mtiles = (rows + BM - 1) / BM;
   const int64_t blocks = (mtiles + 7) / 8 * 8 * (a.n / BN);  // whole groups of 8 row blocks
-  const size_t lds = (size_t)NSTAGE * 2 * BM * BK * sizeof(bf16);
+  const size_t lds = kGemmLds;
   static std::once_flag once[64];
   int dev = 0;
   (void)hipGetDevice(&dev);
   std::call_once(once[dev & 63], [] {
     (void)hipFuncSetAttribute((const void*)ctx_kv_gemm_kernel,
                               hipFuncAttributeMaxDynamicSharedMemorySize,
-                              NSTAGE * 2 * BM * BK * (int)sizeof(bf16));
+                              (int)kGemmLds);
   });
   if (blocks > 0)
     hipLaunchKernelGGL(ctx_kv_gemm_kernel, dim3((unsigned)blocks), dim3(NTG), lds, s, a);
