@@ -2,7 +2,10 @@
 
 Usage: ``python -m block_diffusion_draft_dflash_amd.build``. Every call
 recompiles every source (objects go to ``_build/`` at the repository root,
-the library next to this file).
+the library next to this file). It also links libdflash_phasetrace.so, the
+same library with the block attention compiled with -DDFLASH_PHASE_TRACE
+(per-workgroup phase timestamps; read by ``phase_trace.py``, never by the
+product path).
 """
 from __future__ import annotations
 
@@ -18,6 +21,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libdflash.so")
+TRACE_LIB = os.path.join(PKG, "libdflash_phasetrace.so")
+TRACE_SOURCE = "block_attention.hip"
 SOURCES = ["dflash_api.hip", "rope_qknorm.hip", "block_attention.hip", "context_kv.hip",
            "kv_store.hip", "layer_proj.hip", "propose_prep.hip", "noalloc_scratch.hip"]
 ARCH = "gfx950"
@@ -42,9 +47,11 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libdflash)")
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+def _compile(src: str, verbose: bool, trace: bool = False) -> str:
+    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ("_phasetrace.o" if trace else ".o"))
     extra = [] if src in AGPR_ACC_SOURCES else VGPR_FORM
+    if trace:
+        extra = extra + ["-DDFLASH_PHASE_TRACE"]
     cmd = [_hipcc(), *HIPFLAGS, *extra, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -54,18 +61,25 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out: str, verbose: bool) -> None:
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    jobs = [(s, False) for s in SOURCES] + [(TRACE_SOURCE, True)]
+    with concurrent.futures.ThreadPoolExecutor(max_workers=4) as ex:
+        objs = list(ex.map(lambda j: _compile(j[0], verbose, j[1]), jobs))
+    _link(objs[:len(SOURCES)], LIB, verbose)
+    trace_objs = [o if s != TRACE_SOURCE else objs[-1] for s, o in zip(SOURCES, objs)]
+    _link(trace_objs, TRACE_LIB, verbose)
     return LIB
 
 

@@ -48,6 +48,34 @@ constexpr int KT = 32;     // keys per tile
 constexpr int NT = 256;    // threads per workgroup
 constexpr float LOG2E = 1.4426950408889634f;
 
+// Phase trace (diagnostic build, -DDFLASH_PHASE_TRACE, libdflash_phasetrace.so):
+// every workgroup of both kernels writes one record of 8 u64 to a region at
+// the end of the workspace: the 100 MHz real-time counter at its start, after
+// the unit lookup, at the loop's start and end and at its end, its XCD, its
+// tile count and its kind (1: main kernel, 2: merge kernel). The product
+// build compiles none of it.
+#ifdef DFLASH_PHASE_TRACE
+constexpr bool kPhaseTrace = true;
+#else
+constexpr bool kPhaseTrace = false;
+#endif
+__device__ __forceinline__ uint64_t pt_now() {
+  if constexpr (kPhaseTrace) return __builtin_amdgcn_s_memrealtime();
+  return 0;
+}
+__device__ __forceinline__ void pt_record(uint64_t* rec, uint64_t t0, uint64_t t1, uint64_t t2,
+                                          uint64_t t3, int64_t tiles, int kind) {
+  if constexpr (kPhaseTrace) {
+    if (threadIdx.x == 0) {
+      uint32_t xcc;
+      asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(xcc));
+      const uint64_t t4 = __builtin_amdgcn_s_memrealtime();
+      rec[0] = t0; rec[1] = t1; rec[2] = t2; rec[3] = t3; rec[4] = t4;
+      rec[5] = xcc; rec[6] = (uint64_t)tiles; rec[7] = (uint64_t)kind;
+    }
+  }
+}
+
 // Work split planned on the host from host copies of the lengths, passed
 // by value with the launch (kernel arguments): for each request its rows,
 // visible key range, split size, split count and first unit, and the launch
@@ -101,6 +129,8 @@ struct AttnArgs {
   float eps;
   float scale_log2;
   int32_t causal, window;
+  uint64_t* trace;     // phase-trace records (diagnostic build), else unused
+  int64_t trace_main;  // records of the main kernel (the merge kernel's follow)
   HostSched hs;
 };
 
@@ -430,6 +460,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   // with the plan's counts, all before any branch, and the unit's request is
   // then read from its lane: the unit's numbers arrive after one memory round
   // trip.
+  const uint64_t pt0 = pt_now();
   const int32_t g = blockIdx.x;
   int32_t u = (int32_t)blockIdx.y + 65535 * (int32_t)blockIdx.z;  // canonical unit index
   const int32_t hnreq = a.hs.nreq, hnunits = a.hs.nunits;
@@ -477,6 +508,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   un.first = uni(un.first); un.clen = uni(un.clen); un.blen = uni(un.blen); un.lo = uni(un.lo);
   un.csz = uni(un.csz);
   un.ctx0 = uni(un.ctx0); un.blk0 = uni(un.blk0);
+  const uint64_t pt1 = pt_now();
+  uint64_t* const pt_rec =
+      kPhaseTrace ? a.trace + 8 * (((int64_t)blockIdx.y + 65535 * (int64_t)blockIdx.z) * gridDim.x + blockIdx.x)
+                  : nullptr;
 
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -772,6 +807,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   const int src_row = 4 * j + (m >> 2);
   const int src_col4 = (m & 3) * 4;
 
+  const uint64_t pt2 = pt_now();
   for (int32_t it = 0; it < ntiles; ++it) {
     // Own loads of tile `it` landed (tiles issued after it may stay in flight),
     // then the barrier makes every wave's part visible and frees stage it-1.
@@ -875,6 +911,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 
   const float ltot = xrow4_sum(lsum);
   const int32_t nrow_unit = 16 * w + m;  // row within the unit's query tile
+  const uint64_t pt3 = pt_now();
 
   if (un.nsplit == 1) {
     if (rvalid) {
@@ -888,6 +925,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
         *reinterpret_cast<bf16x4*>(dst + 16 * dt) = o;
       }
     }
+    pt_record(pt_rec, pt0, pt1, pt2, pt3, ntiles, 1);
     return;
   }
 
@@ -928,6 +966,7 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
     if (un.s == 0 && tid == 0 && a.hs.nreq == 0)
       a.dir[((int64_t)un.r * a.qtiles + un.qt) * a.hkv + g] = un.first;
   }
+  pt_record(pt_rec, pt0, pt1, pt2, pt3, ntiles, 1);
 }
 
 // Merge of split partials: one workgroup per (request, query tile, kv-head,
@@ -942,6 +981,7 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
   constexpr int RPW = NT / TPR;           // rows per workgroup pass
   constexpr int MB = 8;
   const int32_t rb_count = QROWS / MROWS;
+  const uint64_t pt0 = pt_now();
   // What the host-planned path needs is read before any branch: the scalar
   // arguments and, lane l, request l's record (zeros past the requests), so
   // one memory round trip precedes the partials' loads.
@@ -1038,6 +1078,7 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
       }
     }
   }
+  pt_record(a.trace + 8 * (a.trace_main + blockIdx.x), pt0, 0, 0, 0, ns, 2);
 }
 
 // ----------------------------------------------------------------------------
@@ -1314,6 +1355,13 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool p
   off = align_up(off + sizeof(uint16_t) * (size_t)pl.units * p.num_kv_heads * QROWS * p.head_dim, 256);
   pl.off_part_ml = off;
   off = align_up(off + sizeof(float) * 4 * (size_t)pl.units * p.num_kv_heads * QROWS, 256);
+  pl.off_trace = off;
+  pl.trace_main = 0;
+  if (kPhaseTrace) {
+    const int64_t mblocks = (int64_t)p.num_reqs * pl.qtiles * p.num_kv_heads * (QROWS / MROWS);
+    pl.trace_main = pl.units * p.num_kv_heads;
+    off += (size_t)64 * (size_t)(pl.trace_main + mblocks);
+  }
   pl.bytes = (p.dtype == DFLASH_BF16) ? off : 0;
   *plan = pl;
   return true;
@@ -1358,6 +1406,8 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   a.units = (int32_t)plan.units;
   a.units_pref = (int32_t)plan.units_pref;
   a.hdr = (int32_t*)w;
+  a.trace = (uint64_t*)(w + plan.off_trace);
+  a.trace_main = plan.trace_main;
   if (pg) {
     a.bt = pg->block_table;
     a.bt_stride = pg->max_pages_per_req;
@@ -1413,3 +1463,17 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
 }
 
 }  // namespace dflash
+
+#ifdef DFLASH_PHASE_TRACE
+// Diagnostic build only: byte offset of the phase-trace records in the
+// workspace of a bf16 call with these parameters, and the number of records of
+// the main kernel (the merge kernel's follow them).
+extern "C" size_t dflash_phase_trace_layout(const dflash_block_attn_params* p, int paged,
+                                            int64_t* main_records, int64_t* merge_records) {
+  dflash::AttnPlan plan;
+  dflash::plan_block_attention(*p, 256, paged != 0, &plan);
+  *main_records = plan.trace_main;
+  *merge_records = (int64_t)((plan.bytes - plan.off_trace) / 64) - plan.trace_main;
+  return plan.off_trace;
+}
+#endif

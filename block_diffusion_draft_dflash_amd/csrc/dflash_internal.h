@@ -24,6 +24,8 @@ struct AttnPlan {
   int64_t units;      // bound on work units per kv-head (grid = units * Hkv)
   int64_t units_pref; // unit budget the split is chosen for first (<= units)
   size_t off_counters, off_part_o, off_part_ml, bytes;
+  size_t off_trace;    // phase-trace records (diagnostic build only; else == bytes)
+  int64_t trace_main;  // records of the main kernel's workgroups (diagnostic build)
 };
 bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool paged,
                           AttnPlan* plan);

@@ -156,6 +156,27 @@ def test_paged_validation(lib):
     assert B.dflash_block_attention_paged_workspace_size(P(split_keys=32768)) == 0
 
 
+def test_phase_trace_build(lib):
+    # the diagnostic build appends its records to the product workspace layout
+    # and is the only library exporting the layout query
+    from block_diffusion_draft_dflash_amd.build import TRACE_LIB
+    assert not hasattr(lib, "dflash_phase_trace_layout")
+    tr = ctypes.CDLL(TRACE_LIB)
+    f = tr.dflash_phase_trace_layout
+    f.restype = ctypes.c_size_t
+    f.argtypes = [ctypes.POINTER(B.BlockAttnParams), ctypes.c_int, ctypes.POINTER(ctypes.c_int64),
+                  ctypes.POINTER(ctypes.c_int64)]
+    tr.dflash_block_attention_workspace_size.restype = ctypes.c_size_t
+    tr.dflash_block_attention_workspace_size.argtypes = [ctypes.POINTER(B.BlockAttnParams)]
+    for kw in (dict(), dict(num_reqs=64, total_ctx=64 * 3000, total_blk=64 * 16), dict(split_keys=128)):
+        p = P(**kw)
+        nm, ng = ctypes.c_int64(), ctypes.c_int64()
+        off = f(ctypes.byref(p), 0, ctypes.byref(nm), ctypes.byref(ng))
+        assert off == B.dflash_block_attention_workspace_size(p)
+        assert nm.value >= 8 and ng.value == p.num_reqs * 8 * 4
+        assert tr.dflash_block_attention_workspace_size(ctypes.byref(p)) == off + 64 * (nm.value + ng.value)
+
+
 def test_kv_scatter_validation(lib):
     f = lib.dflash_kv_scatter
     assert f(7, None, None, None, 4, 8, 128, None, None, 64, None) == B.DFLASH_ERR_INVALID_ARG
