@@ -12,14 +12,15 @@
 // bf16, the reference rounds the normed activations instead) and 1/rms_t is
 // applied in the GEMM epilogue; the GEMM computes it from the A fragments
 // its waves already hold (no separate pass over the hidden states). The GEMM
-// (M = rows, N = 2 * Hkv * Dh, K = H) runs on v_mfma_f32_16x16x32_bf16 with
-// 256x256 workgroup tiles of 4 waves (one per SIMD); a wave owns 128 rows x
-// one whole 128-wide head, so the k-norm and the rotate-half pairs (d, d + 64)
-// stay inside the wave. The k-slices of A and B are copied HBM -> LDS
-// directly (no register staging) up to NSTAGE - 1 slices ahead, with explicit
-// waits and fence-free barriers, and each wave reads the next slice's
-// fragments while the MFMAs of the current one run. The epilogue stages each
-// wave's bf16 tile in LDS and writes whole 16-byte pieces of the output rows.
+// (M = rows, N = 2 * Hkv * Dh, K = H) runs on v_mfma_f32_32x32x16_bf16 with
+// its accumulators in AGPRs, in 256x256 workgroup tiles of 4 waves (one per
+// SIMD); a wave owns 128 rows x one whole 128-wide head, so the k-norm and
+// the rotate-half pairs (d, d + 64) stay inside the wave. The 64-wide
+// k-slices of A and B are copied HBM -> LDS directly (no register staging),
+// the next slice in flight while the current one is consumed, with explicit
+// waits and one fence-free barrier per slice; each wave's fragment reads are
+// interleaved with its MFMAs. The epilogue stages each wave's bf16 tile in
+// LDS and writes whole 16-byte pieces of the output rows.
 #include <mutex>
 
 #include "dflash_device.h"
