@@ -160,6 +160,11 @@ EDGE = {
                                  blk_lens=[3, 0, 17, 40, 1]),
     "gqa1": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=200, hq=8, hkv=8),
     "gqa8": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=200, hq=64, hkv=8),
+    # group 2; one kv-head (all q-heads share it); group 16 (four 64-row query
+    # tiles per request and kv-head)
+    "gqa2": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=50, ctx_hi=400, hq=16, hkv=8),
+    "mqa": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=50, ctx_hi=400, hq=8, hkv=1),
+    "gqa16": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=100, ctx_hi=600, hq=64, hkv=4),
     "dh64_bf16": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=50, ctx_hi=300, hq=8, hkv=2, dh=64),
     "causal_nowindow": dict(name="swa", num_reqs=3, ctx_len=200, window=0),
     "window1": dict(name="swa", num_reqs=2, ctx_len=100, window=1),
@@ -180,7 +185,7 @@ def test_parity_edges(case):
 
 
 @pytest.mark.parametrize("case", ["empty_ctx_and_blocks", "dh64_bf16", "causal_long_block",
-                                  "window1"])
+                                  "window1", "mqa", "gqa16"])
 def test_parity_edges_device_planned(case):
     # the work split derived by the kernels from the device lengths alone
     print(f"case edge device-planned {case}", flush=True)
@@ -235,6 +240,8 @@ FUSED = {
                                  blk_lens=[64, 64, 34, 64]),
     "dh64": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=50, ctx_hi=300, hq=8, hkv=2, dh=64),
     "gqa8": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=50, ctx_hi=200, hq=64, hkv=8),
+    "mqa": dict(name="qwen3_8b_draft", num_reqs=3, ctx_lo=50, ctx_hi=400, hq=8, hkv=1),
+    "gqa16": dict(name="qwen3_8b_draft", num_reqs=2, ctx_lo=100, ctx_hi=600, hq=64, hkv=4),
 }
 
 
