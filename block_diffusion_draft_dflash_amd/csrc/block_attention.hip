@@ -337,7 +337,16 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
-constexpr int NSTAGE = 4;  // LDS stages: NSTAGE - 1 tiles in flight
+// LDS stages of the main kernel (NSTAGE - 1 tiles in flight). A launch of
+// one round of two workgroups per CU runs 3 (four tiles in flight per CU;
+// measured 96.9 vs 99.1 us on 4 x 32768 context rows and 56.4 vs 57.1 us on
+// the 16-request sliding-window batch); one workgroup per CU (fewer units) or
+// several rounds (many requests) run 4 (3 stages measured 20.1 vs 19.8 and
+// 115.1 vs 113.6 us there), and so does any block that may span three tiles:
+// the fused prologue normalises the block's K rows in the stages of its first
+// tiles before the loop.
+constexpr int NSTAGE_MAX = 4;
+constexpr int MAX_BLK_3STAGE = KT + 1;  // block rows that span at most two tiles
 
 // s_waitcnt takes an immediate: wait until at most k * STEP vector-memory
 // operations are outstanding, for a run-time k (clamped to [0, MAXK]).
@@ -440,7 +449,7 @@ __device__ __forceinline__ int32_t clamp_pos(int32_t p, int32_t max_pos) {
 // VGPRs per wave are free; saying so keeps the compiler from spilling to
 // stay under the 4-wave budget (a scratch reload inside the loop would wait
 // for every tile copy in flight).
-template <int DH, bool FUSE>
+template <int DH, bool FUSE, int NSTAGE>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void block_attn_bf16_kernel(AttnArgs a) {
   constexpr int CH = DH / 8;                 // 16-byte chunks per row
   constexpr int DS = DH / 32;                // MFMA k-steps over the head dim
@@ -774,7 +783,8 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
 #pragma unroll
     for (int ds = 0; ds < DS; ++ds) qf[ds] = rvalid ? qn[ds] : bf16x8{};
     // block K rows: in place in the LDS stages of the first tiles (at most
-    // NSTAGE - 1 of them hold block keys: max_blk_len <= 2 KT is required).
+    // NSTAGE - 1 of them hold block keys: the host picks NSTAGE for the
+    // longest block).
     if (nblk > 0) {
       wait_lgkm0();
       block_barrier();
@@ -1309,6 +1319,7 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool p
                           AttnPlan* plan) {
   AttnPlan pl{};
   pl.group = p.num_q_heads / p.num_kv_heads;
+  pl.cus = num_cus > 0 ? num_cus : 256;
   const int64_t qt = ((int64_t)pl.group * p.max_blk_len + QROWS - 1) / QROWS;
   pl.qtiles = (int32_t)(qt < 1 ? 1 : qt);
   int64_t eff = p.total_ctx + p.total_blk;
@@ -1429,34 +1440,53 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   // Host-planned: launch only the units the plan uses.
   const int64_t blocks = (a.hs.nreq > 0 ? a.hs.nunits : plan.units) * p.num_kv_heads;
   if (blocks == 0) return hipSuccess;
-  const size_t lds = (size_t)NSTAGE * 2 * KT * p.head_dim * sizeof(bf16) + (PG_MAX + POS_LDS) * sizeof(int32_t);
+  const int64_t cus = plan.cus;
+  const int nstage =
+      (p.max_blk_len <= MAX_BLK_3STAGE && blocks > cus && blocks <= 2 * cus) ? 3 : 4;
+  const size_t lds = (size_t)nstage * 2 * KT * p.head_dim * sizeof(bf16) +
+                     (PG_MAX + POS_LDS) * sizeof(int32_t);
   // The LDS limit attribute is a per-function setting: raise it once per
   // device (not per launch, so that stream capture sees only the launch).
   static std::once_flag once[64];
   int dev = 0;
   (void)hipGetDevice(&dev);
   std::call_once(once[dev & 63], [] {
-    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2 + (PG_MAX + POS_LDS) * 4);
-    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<128, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 128 * 2 + (PG_MAX + POS_LDS) * 4);
-    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64, false>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + (PG_MAX + POS_LDS) * 4);
-    (void)hipFuncSetAttribute((const void*)block_attn_bf16_kernel<64, true>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, NSTAGE * 2 * KT * 64 * 2 + (PG_MAX + POS_LDS) * 4);
+    constexpr int extra = (PG_MAX + POS_LDS) * 4;
+    constexpr int s128 = NSTAGE_MAX * 2 * KT * 128 * 2 + extra, s64 = NSTAGE_MAX * 2 * KT * 64 * 2 + extra;
+    const void* fns[8] = {(const void*)block_attn_bf16_kernel<128, false, 3>,
+                          (const void*)block_attn_bf16_kernel<128, true, 3>,
+                          (const void*)block_attn_bf16_kernel<128, false, 4>,
+                          (const void*)block_attn_bf16_kernel<128, true, 4>,
+                          (const void*)block_attn_bf16_kernel<64, false, 3>,
+                          (const void*)block_attn_bf16_kernel<64, true, 3>,
+                          (const void*)block_attn_bf16_kernel<64, false, 4>,
+                          (const void*)block_attn_bf16_kernel<64, true, 4>};
+    for (int i = 0; i < 8; ++i)
+      (void)hipFuncSetAttribute(fns[i], hipFuncAttributeMaxDynamicSharedMemorySize, i < 4 ? s128 : s64);
   });
   const int64_t mblocks = (int64_t)p.num_reqs * plan.qtiles * p.num_kv_heads * (QROWS / MROWS);
   const int64_t launch_units = blocks / p.num_kv_heads;
   const dim3 grid((unsigned)p.num_kv_heads, (unsigned)std::min<int64_t>(launch_units, 65535),
                   (unsigned)((launch_units + 65534) / 65535));
   const dim3 blk(NT), mgrid((unsigned)mblocks);
+  auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, blk, lds, s, a); };
   if (p.head_dim == 128) {
-    if (pro) hipLaunchKernelGGL((block_attn_bf16_kernel<128, true>), grid, blk, lds, s, a);
-    else hipLaunchKernelGGL((block_attn_bf16_kernel<128, false>), grid, blk, lds, s, a);
+    if (nstage == 3) {
+      if (pro) launch_main(block_attn_bf16_kernel<128, true, 3>);
+      else launch_main(block_attn_bf16_kernel<128, false, 3>);
+    } else {
+      if (pro) launch_main(block_attn_bf16_kernel<128, true, 4>);
+      else launch_main(block_attn_bf16_kernel<128, false, 4>);
+    }
     hipLaunchKernelGGL(block_attn_merge_kernel<128>, mgrid, blk, 0, s, a);
   } else {
-    if (pro) hipLaunchKernelGGL((block_attn_bf16_kernel<64, true>), grid, blk, lds, s, a);
-    else hipLaunchKernelGGL((block_attn_bf16_kernel<64, false>), grid, blk, lds, s, a);
+    if (nstage == 3) {
+      if (pro) launch_main(block_attn_bf16_kernel<64, true, 3>);
+      else launch_main(block_attn_bf16_kernel<64, false, 3>);
+    } else {
+      if (pro) launch_main(block_attn_bf16_kernel<64, true, 4>);
+      else launch_main(block_attn_bf16_kernel<64, false, 4>);
+    }
     hipLaunchKernelGGL(block_attn_merge_kernel<64>, mgrid, blk, 0, s, a);
   }
   return hipGetLastError();

@@ -26,6 +26,7 @@ struct AttnPlan {
   size_t off_counters, off_part_o, off_part_ml, bytes;
   size_t off_trace;    // phase-trace records (diagnostic build only; else == bytes)
   int64_t trace_main;  // records of the main kernel's workgroups (diagnostic build)
+  int32_t cus;         // compute units the plan was made for
 };
 bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool paged,
                           AttnPlan* plan);
