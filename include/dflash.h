@@ -52,7 +52,16 @@ typedef enum {
   DFLASH_ERR_HIP = -4          /* the HIP runtime reported an error */
 } dflash_status;
 
-typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
+/* The two range markers are not data types: they make every 32-bit value a
+ * valid dflash_dtype in C++ as in C, so that the library can reject any value
+ * a caller passes (DFLASH_ERR_INVALID_ARG) without reading an out-of-range
+ * enumeration value. */
+typedef enum {
+  DFLASH_F32 = 0,
+  DFLASH_BF16 = 1,
+  DFLASH_DTYPE_RANGE_MIN_ = -0x7fffffff - 1,
+  DFLASH_DTYPE_RANGE_MAX_ = 0x7fffffff
+} dflash_dtype;
 
 /* Message of the last failed call on this thread ("" if none). Never NULL. */
 const char* dflash_last_error(void);
