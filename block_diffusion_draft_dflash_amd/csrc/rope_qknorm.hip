@@ -26,36 +26,42 @@ __global__ void rope_table_kernel(float2* __restrict__ table, int32_t max_pos, i
   table[idx] = make_float2((float)c, (float)s);
 }
 
+// 16 bytes of T: the unit each lane loads and stores.
 template <typename T>
-struct Vec4;
+struct Piece;
 template <>
-struct Vec4<bf16> {
-  typedef bf16x4 type;
-  static __device__ __forceinline__ void load(const bf16* p, float* x) {
-    bf16x4 v = *reinterpret_cast<const bf16x4*>(p);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = bf2f(v[e]);
-  }
+struct Piece<bf16> {
+  static constexpr int N = 8;
+  typedef bf16x8 raw;
+  static __device__ __forceinline__ raw load(const bf16* p) { return *reinterpret_cast<const bf16x8*>(p); }
+  static __device__ __forceinline__ float get(const raw& v, int e) { return bf2f(v[e]); }
   static __device__ __forceinline__ void store(bf16* p, const float* x) {
-    bf16x4 v;
+    bf16x8 v;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) v[e] = f2bf(x[e]);
-    *reinterpret_cast<bf16x4*>(p) = v;
+    for (int e = 0; e < 8; ++e) v[e] = f2bf(x[e]);
+    *reinterpret_cast<bf16x8*>(p) = v;
   }
 };
 template <>
-struct Vec4<float> {
-  static __device__ __forceinline__ void load(const float* p, float* x) {
-    float4 v = *reinterpret_cast<const float4*>(p);
-    x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
-  }
+struct Piece<float> {
+  static constexpr int N = 4;
+  typedef f32x4 raw;
+  static __device__ __forceinline__ raw load(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
+  static __device__ __forceinline__ float get(const raw& v, int e) { return v[e]; }
   static __device__ __forceinline__ void store(float* p, const float* x) {
-    *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
   }
 };
 
-// One head vector per group of DH/8 lanes. Lane s of the group holds elements
-// [4s, 4s+4) of the first half and their rotation partners [DH/2+4s, DH/2+4s+4).
+constexpr int HC = 8;  // heads of one row per lane group
+
+// One lane group of LANES = (DH/2) / (elements per 16 bytes) lanes takes one
+// row and up to HC of its heads (q heads first, then k heads). Lane s holds
+// elements [N s, N s + N) of each head's first half and their rotation
+// partners DH/2 further on, so it needs the cos/sin of N frequencies only:
+// those are read once per row and chunk of heads rather than once per head
+// vector (per head they would be twice the bytes of the vector itself), and
+// each lane has all of its heads' loads in flight together.
 template <typename T, int DH>
 __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
     T* __restrict__ q, T* __restrict__ k, const float* __restrict__ wq,
@@ -65,51 +71,84 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(
   // every argument in one batch of scalar loads (no dependent argument reads)
   asm volatile("" ::"s"(q), "s"(k), "s"(wq), "s"(wk), "s"(pos), "s"(table), "s"(max_pos), "s"(rows),
                "s"(hq), "s"(hkv), "s"(eps));
-  constexpr int LANES = DH / 8;
-  constexpr int PER_WAVE = 64 / LANES;
+  constexpr int N = Piece<T>::N;
   constexpr int HALF = DH / 2;
+  constexpr int LANES = HALF / N;
+  constexpr int GPW = 64 / LANES;  // lane groups per wave
   const int lane = threadIdx.x & 63;
   const int s = lane % LANES;
-  const int64_t vec = ((int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) * PER_WAVE +
-                      lane / LANES;
+  const int64_t grp =
+      ((int64_t)blockIdx.x * (blockDim.x / 64) + threadIdx.x / 64) * GPW + lane / LANES;
   const int32_t hq_eff = q ? hq : 0;
   const int32_t heads = hq_eff + hkv;
-  const bool valid = vec < rows * heads;
-  const int64_t row = valid ? vec / heads : 0;
-  const int32_t h = valid ? (int32_t)(vec % heads) : 0;
-  T* base = (h < hq_eff) ? q + (row * hq + h) * DH : k + (row * hkv + (h - hq_eff)) * DH;
-  const float* w = (h < hq_eff) ? wq : wk;
+  const int32_t chunks = (heads + HC - 1) / HC;
+  // whole lane groups leave together, so the group reductions below only
+  // ever read lanes that are still running
+  if (grp >= rows * chunks) return;
+  const int64_t row = grp / chunks;
+  const int32_t h0 = (int32_t)(grp - row * chunks) * HC;
+  const int32_t p = pos[row];
 
-  float x0[4] = {0.f, 0.f, 0.f, 0.f}, x1[4] = {0.f, 0.f, 0.f, 0.f};
-  if (valid) {
-    Vec4<T>::load(base + 4 * s, x0);
-    Vec4<T>::load(base + HALF + 4 * s, x1);
-  }
-  float ss = 0.f;
+  typename Piece<T>::raw x0[HC], x1[HC];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) ss += x0[e] * x0[e] + x1[e] * x1[e];
-  ss = group_sum<LANES>(ss);  // all lanes of a group share `valid`
-  const float inv = 1.0f / sqrtf(ss * (1.0f / DH) + eps);
-  if (!valid) return;
-  int32_t p = pos[row];
-  p = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
-  const float4* cs4 = reinterpret_cast<const float4*>(table + (int64_t)p * HALF + 4 * s);
-  const float4 c01 = cs4[0], c23 = cs4[1];
-  const float cs[8] = {c01.x, c01.y, c01.z, c01.w, c23.x, c23.y, c23.z, c23.w};
-  const float4 w0 = *reinterpret_cast<const float4*>(w + 4 * s);
-  const float4 w1 = *reinterpret_cast<const float4*>(w + HALF + 4 * s);
-  const float wa[4] = {w0.x, w0.y, w0.z, w0.w}, wb[4] = {w1.x, w1.y, w1.z, w1.w};
-  float y0[4], y1[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    const float a = x0[e] * inv * wa[e];
-    const float b = x1[e] * inv * wb[e];
-    const float c = cs[2 * e], sn = cs[2 * e + 1];
-    y0[e] = a * c - b * sn;
-    y1[e] = b * c + a * sn;
+  for (int i = 0; i < HC; ++i) {
+    // heads past the row's last re-read its last head and store nothing
+    const int32_t h = min(h0 + i, heads - 1);
+    const T* src = (h < hq_eff) ? q + (row * hq + h) * DH : k + (row * hkv + (h - hq_eff)) * DH;
+    x0[i] = Piece<T>::load(src + N * s);
+    x1[i] = Piece<T>::load(src + HALF + N * s);
   }
-  Vec4<T>::store(base + 4 * s, y0);
-  Vec4<T>::store(base + HALF + 4 * s, y1);
+  float wa[2][N], wb[2][N];  // [q | k] weights of this lane's elements
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const float* w = t == 0 ? wq : wk;
+    const bool need = t == 0 ? h0 < hq_eff : h0 + HC > hq_eff;
+#pragma unroll
+    for (int e4 = 0; e4 < N / 4; ++e4) {
+      const float4 v0 = need ? *reinterpret_cast<const float4*>(w + N * s + 4 * e4) : float4{};
+      const float4 v1 = need ? *reinterpret_cast<const float4*>(w + HALF + N * s + 4 * e4) : float4{};
+      wa[t][4 * e4] = v0.x; wa[t][4 * e4 + 1] = v0.y; wa[t][4 * e4 + 2] = v0.z; wa[t][4 * e4 + 3] = v0.w;
+      wb[t][4 * e4] = v1.x; wb[t][4 * e4 + 1] = v1.y; wb[t][4 * e4 + 2] = v1.z; wb[t][4 * e4 + 3] = v1.w;
+    }
+  }
+  const int32_t pc = p < 0 ? 0 : (p >= max_pos ? max_pos - 1 : p);
+  const float4* cs4 = reinterpret_cast<const float4*>(table + (int64_t)pc * HALF + N * s);
+  float cs[2 * N];
+#pragma unroll
+  for (int e2 = 0; e2 < N / 2; ++e2) {
+    const float4 c = cs4[e2];
+    cs[4 * e2] = c.x; cs[4 * e2 + 1] = c.y; cs[4 * e2 + 2] = c.z; cs[4 * e2 + 3] = c.w;
+  }
+
+#pragma unroll
+  for (int i = 0; i < HC; ++i) {
+    const int32_t h = h0 + i;
+    float a[N], b[N];
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      a[e] = Piece<T>::get(x0[i], e);
+      b[e] = Piece<T>::get(x1[i], e);
+      ss += a[e] * a[e] + b[e] * b[e];
+    }
+    ss = group_sum<LANES>(ss);
+    const float inv = 1.0f / sqrtf(ss * (1.0f / DH) + eps);
+    const int t = h < hq_eff ? 0 : 1;
+    float y0[N], y1[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) {
+      const float u = a[e] * inv * wa[t][e];
+      const float v = b[e] * inv * wb[t][e];
+      const float c = cs[2 * e], sn = cs[2 * e + 1];
+      y0[e] = u * c - v * sn;
+      y1[e] = v * c + u * sn;
+    }
+    if (h < heads) {
+      T* dst = (h < hq_eff) ? q + (row * hq + h) * DH : k + (row * hkv + (h - hq_eff)) * DH;
+      Piece<T>::store(dst + N * s, y0);
+      Piece<T>::store(dst + HALF + N * s, y1);
+    }
+  }
 }
 
 template <typename T, int DH>
@@ -117,9 +156,10 @@ hipError_t launch_qknr(T* q, T* k, const float* wq, const float* wk, const int32
                        int64_t rows, int32_t hq, int32_t hkv, float eps, const float* table,
                        int32_t max_pos, hipStream_t s) {
   const int64_t heads = (q ? hq : 0) + hkv;
-  const int64_t vecs = rows * heads;
-  const int64_t per_block = 4 * (64 / (DH / 8));
-  const int64_t blocks = (vecs + per_block - 1) / per_block;
+  const int64_t groups = rows * ((heads + HC - 1) / HC);
+  const int64_t per_block = 4 * (64 / (DH / 2 / Piece<T>::N));
+  const int64_t blocks = (groups + per_block - 1) / per_block;
+  if (blocks == 0) return hipGetLastError();
   hipLaunchKernelGGL((qk_norm_rope_kernel<T, DH>), dim3((unsigned)blocks), dim3(256), 0, s, q, k,
                      wq, wk, pos, reinterpret_cast<const float2*>(table), max_pos, rows, hq, hkv,
                      eps);
