@@ -3,11 +3,17 @@
 // Host checks mirror the preconditions the "qwen3_dflash.cpp" page enforces
 // with VT_CHECK (num_reqs > 0, cumulative lengths spanning the rows, matching
 // sizes), turned into status codes plus a per-thread message instead of
-// exceptions. Nothing here allocates device memory or synchronises.
+// exceptions. Nothing here allocates device memory or synchronises, except in
+// the DFLASH_VALIDATE debug mode (below), which copies device-resident
+// metadata to the host and waits for it.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "dflash_internal.h"
 
@@ -56,6 +62,73 @@ dflash_status check_head_geometry(int32_t hq, int32_t hkv, int32_t dh, bool need
   return DFLASH_OK;
 }
 
+// ---------------------------------------------------------------------------
+// DFLASH_VALIDATE debug mode. With the environment variable set (to anything
+// but "" or "0"; read at every call), the calls that take integer metadata on
+// the device copy it to the host on their stream, wait for it, and check it
+// before enqueueing anything: the same preconditions the reference checks on
+// the host, which the kernels otherwise trust (and only clamp).
+bool validate_enabled() {
+  const char* v = std::getenv("DFLASH_VALIDATE");
+  return v && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
+
+// n int32 values from the device into out (synchronises the stream).
+dflash_status fetch_i32(const char* who, const char* what, const int32_t* dev, int64_t n,
+                        std::vector<int32_t>* out, void* stream) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing((hipStream_t)stream, &cs) == hipSuccess && cs != hipStreamCaptureStatusNone)
+    return fail(DFLASH_ERR_UNSUPPORTED,
+                "%s: DFLASH_VALIDATE waits for the stream and cannot run while it is captured", who);
+  out->assign((size_t)n, 0);
+  if (n == 0) return DFLASH_OK;
+  if (!dev) return fail(DFLASH_ERR_INVALID_ARG, "%s: %s is NULL", who, what);
+  hipError_t e = hipMemcpyAsync(out->data(), dev, (size_t)n * sizeof(int32_t), hipMemcpyDeviceToHost,
+                                (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess)
+    return fail(DFLASH_ERR_HIP, "%s: DFLASH_VALIDATE could not read %s: HIP error %d (%s)", who, what,
+                (int)e, hipGetErrorString(e));
+  return DFLASH_OK;
+}
+
+// Cumulative lengths: c[0] == 0, nondecreasing, c[R] == total; optionally each
+// length <= max_len and equal to the host copy.
+dflash_status check_cu(const char* who, const char* what, const std::vector<int32_t>& c, int64_t total,
+                       int32_t max_len, const int32_t* host) {
+  const size_t r_count = c.size() - 1;
+  if (c[0] != 0) return fail(DFLASH_ERR_INVALID_ARG, "%s: %s[0] = %d, expected 0", who, what, c[0]);
+  for (size_t r = 0; r < r_count; ++r) {
+    if (c[r + 1] < c[r])
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: %s decreases at request %zu (%d -> %d)", who, what, r,
+                  c[r], c[r + 1]);
+    if (max_len >= 0 && c[r + 1] - c[r] > max_len)
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: request %zu has %d rows in %s, more than %d", who, r,
+                  c[r + 1] - c[r], what, max_len);
+  }
+  if (c[r_count] != total)
+    return fail(DFLASH_ERR_INVALID_ARG, "%s: %s ends at %d, expected %lld", who, what, c[r_count],
+                (long long)total);
+  if (host)
+    for (size_t r = 0; r <= r_count; ++r)
+      if (host[r] != c[r])
+        return fail(DFLASH_ERR_INVALID_ARG, "%s: device %s[%zu] = %d differs from the host copy (%d)",
+                    who, what, r, c[r], host[r]);
+  return DFLASH_OK;
+}
+
+dflash_status check_positions(const char* who, const int32_t* dev, int64_t n, int32_t max_pos,
+                              void* stream) {
+  std::vector<int32_t> pos;
+  dflash_status st = fetch_i32(who, "positions", dev, n, &pos, stream);
+  if (st != DFLASH_OK) return st;
+  for (int64_t i = 0; i < n; ++i)
+    if (pos[(size_t)i] < 0 || pos[(size_t)i] >= max_pos)
+      return fail(DFLASH_ERR_INVALID_ARG, "%s: positions[%lld] = %d is outside [0, %d)", who,
+                  (long long)i, pos[(size_t)i], max_pos);
+  return DFLASH_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -97,6 +170,10 @@ dflash_status dflash_qk_norm_rope(dflash_dtype dtype, void* q, void* k, const fl
       (q && !aligned(q_norm_w, 16)) || !aligned(rope_table, 16))
     return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: tensors must be 16-byte aligned");
   if (T > (int64_t)1 << 40) return fail(DFLASH_ERR_INVALID_ARG, "qk_norm_rope: T too large");
+  if (validate_enabled()) {
+    st = check_positions("qk_norm_rope", positions, T, max_pos, stream);
+    if (st != DFLASH_OK) return st;
+  }
   return hip_status(dflash::launch_qk_norm_rope(dtype, q, k, q_norm_w, k_norm_w, positions, T,
                                                 num_q_heads, num_kv_heads, head_dim, eps,
                                                 rope_table, max_pos, (hipStream_t)stream),
@@ -235,6 +312,34 @@ dflash_status block_attention_impl(const char* who, const dflash_block_attn_para
   }
   if (plan.units * p->num_kv_heads > INT32_MAX)
     return fail(DFLASH_ERR_UNSUPPORTED, "%s: too many work units", who);
+  if (validate_enabled()) {
+    std::vector<int32_t> cc, cb;
+    st = fetch_i32(who, "cu_ctx_lens", cu_ctx_lens, (int64_t)p->num_reqs + 1, &cc, stream);
+    if (st == DFLASH_OK) st = fetch_i32(who, "cu_blk_lens", cu_blk_lens, (int64_t)p->num_reqs + 1, &cb, stream);
+    if (st == DFLASH_OK) st = check_cu(who, "cu_ctx_lens", cc, p->total_ctx, -1, p->host_cu_ctx_lens);
+    if (st == DFLASH_OK)
+      st = check_cu(who, "cu_blk_lens", cb, p->total_blk, p->max_blk_len, p->host_cu_blk_lens);
+    if (st == DFLASH_OK && prologue)
+      st = check_positions(who, prologue->positions, p->total_blk, prologue->max_pos, stream);
+    if (st == DFLASH_OK && pg && p->total_ctx > 0) {
+      std::vector<int32_t> bt;
+      st = fetch_i32(who, "block_table", pg->block_table,
+                     (int64_t)p->num_reqs * pg->max_pages_per_req, &bt, stream);
+      for (int32_t r = 0; st == DFLASH_OK && r < p->num_reqs; ++r) {
+        const int64_t pages = ((int64_t)cc[r + 1] - cc[r] + pg->page_size - 1) / pg->page_size;
+        if (pages > pg->max_pages_per_req)
+          st = fail(DFLASH_ERR_INVALID_ARG, "%s: request %d needs %lld pages, more than max_pages_per_req %d",
+                    who, r, (long long)pages, pg->max_pages_per_req);
+        for (int64_t i = 0; st == DFLASH_OK && i < pages; ++i) {
+          const int32_t id = bt[(size_t)((int64_t)r * pg->max_pages_per_req + i)];
+          if (id < 0 || id >= pg->num_pages)
+            st = fail(DFLASH_ERR_INVALID_ARG, "%s: block_table[%d][%lld] = %d is outside [0, %lld)", who,
+                      r, (long long)i, id, (long long)pg->num_pages);
+        }
+      }
+    }
+    if (st != DFLASH_OK) return st;
+  }
   return hip_status(dflash::launch_block_attention(*p, plan, prologue, pg, cu_ctx_lens, cu_blk_lens,
                                                    q, k_blk, v_blk, k_ctx, v_ctx, out, workspace,
                                                    (hipStream_t)stream),
@@ -314,6 +419,18 @@ dflash_status dflash_kv_scatter(dflash_dtype dtype, const void* k_src, const voi
     return fail(DFLASH_ERR_INVALID_ARG, "kv_scatter: tensors must be 16-byte aligned");
   if (T > ((int64_t)1 << 40) || num_slots > ((int64_t)1 << 40))
     return fail(DFLASH_ERR_INVALID_ARG, "kv_scatter: too many rows");
+  if (validate_enabled()) {
+    std::vector<int32_t> slots;
+    const dflash_status st = fetch_i32("kv_scatter", "slot_mapping", slot_mapping, T, &slots, stream);
+    if (st != DFLASH_OK) return st;
+    std::vector<int32_t> in_range;
+    for (int32_t v : slots)
+      if (v >= 0 && v < num_slots) in_range.push_back(v);
+    std::sort(in_range.begin(), in_range.end());
+    const auto dup = std::adjacent_find(in_range.begin(), in_range.end());
+    if (dup != in_range.end())
+      return fail(DFLASH_ERR_INVALID_ARG, "kv_scatter: slot %d is written by more than one row", *dup);
+  }
   return hip_status(dflash::launch_kv_scatter(dtype, k_src, v_src, slot_mapping, T, num_kv_heads,
                                               head_dim, k_pool, v_pool, num_slots,
                                               (hipStream_t)stream),
@@ -369,6 +486,10 @@ dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, 
   if (T < kCtxKvRowsPath && hidden_size > 8192)
     return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: calls of fewer than %lld rows need hidden_size <= 8192",
                 (long long)kCtxKvRowsPath);
+  if (validate_enabled()) {
+    const dflash_status st = check_positions("context_kv", positions, T, max_pos, stream);
+    if (st != DFLASH_OK) return st;
+  }
   if (T < kCtxKvRowsPath)
     return hip_status(dflash::launch_context_kv_rows(hidden, hidden_norm_w, w_k, w_v, k_norm_w,
                                                      positions, T, hidden_size, num_kv_heads,

@@ -20,7 +20,8 @@
  *     accumulate in f32).
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
  *     call only enqueues work on it: no host synchronisation, no allocation,
- *     so the calls may be captured into a HIP graph.
+ *     so the calls may be captured into a HIP graph (the DFLASH_VALIDATE debug
+ *     mode below is the one exception).
  *   - The caller owns every buffer (inputs, outputs, workspaces). The library
  *     keeps no state between calls.
  *   - Errors: a call returns a negative dflash_status and leaves a message for
@@ -30,6 +31,21 @@
  *     the host-side sizes; kernels clamp every index they derive from it to the
  *     buffers' extents, so inconsistent metadata gives wrong results, never an
  *     out-of-bounds access.
+ *   - Debug mode: with the environment variable DFLASH_VALIDATE set to a value
+ *     other than "" or "0" (read at every call), the calls that take integer
+ *     metadata on the device first copy it to the host on their stream, wait
+ *     for it, and return DFLASH_ERR_INVALID_ARG, naming the first offending
+ *     entry, before anything is enqueued if it breaks a precondition that the
+ *     pages check on the host: block attention (all three forms): cumulative
+ *     lengths start at 0, never decrease, end at total_ctx / total_blk, no
+ *     request has more than max_blk_len block rows, and they equal the host
+ *     copies when those are given; the fused prologue's positions lie in
+ *     [0, max_pos); over a paged store, every page a request's context needs
+ *     fits max_pages_per_req and its id lies in [0, num_pages).
+ *     dflash_qk_norm_rope and dflash_context_kv: positions in [0, max_pos).
+ *     dflash_kv_scatter: no two rows write the same slot. This mode waits for
+ *     the stream, so on a stream that is being captured these calls return
+ *     DFLASH_ERR_UNSUPPORTED.
  *
  * Head geometry: Hq query heads, Hkv key/value heads (Hq % Hkv == 0), head
  * dimension Dh in {64, 128}. q-head h reads kv-head h / (Hq / Hkv).

@@ -12,6 +12,7 @@ out-of-bounds access or undefined behaviour in the validation and planning code
 aborts the process with the sanitizer's report."""
 import ctypes
 import itertools
+import os
 import sys
 
 import numpy as np
@@ -78,6 +79,8 @@ for kw in [dict(), dict(num_reqs=0), dict(num_q_heads=30), dict(num_kv_heads=0),
 # host-planned batches: random varlen requests up to the host table's 64, with
 # empty contexts and blocks, windows, forced splits and more units than the table
 for trial in range(400):
+    # every other batch in the DFLASH_VALIDATE mode (its device reads fail here)
+    os.environ["DFLASH_VALIDATE"] = "1" if trial % 2 else "0"
     r = int(rng.integers(1, 80))
     ctx = rng.integers(0, 9000, r) * (rng.random(r) > 0.1)
     blk = rng.integers(0, 65, r) * (rng.random(r) > 0.1)
@@ -101,7 +104,9 @@ for trial in range(400):
     lib.dflash_block_attention_noalloc(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                        FAKE, None)
 
-# the other entry points' planners and checks
+os.environ["DFLASH_VALIDATE"] = "0"
+
+# the other entry points' planners and checks (then once more in the DFLASH_VALIDATE mode)
 for t, h in itertools.product([0, 1, 5, 128, 255, 256, 1000, 4096], [64, 512, 4096, 8192]):
     lib.dflash_context_kv_workspace_size(t, h, 8, 128)
     lib.dflash_context_kv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, t, h, 8, 128, ctypes.c_float(1e-6), FAKE,
@@ -118,6 +123,15 @@ for t, h in itertools.product([0, 1, 5, 128, 255, 256, 1000, 4096], [64, 512, 40
                             ctypes.c_float(1e-6), FAKE, 4096, None)
     lib.dflash_kv_scatter(B.DFLASH_BF16, FAKE, FAKE, FAKE, t, 8, 128, FAKE, FAKE, 100000, None)
     calls += 10
+os.environ["DFLASH_VALIDATE"] = "1"
+for t in (1, 300):
+    lib.dflash_qk_norm_rope(B.DFLASH_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, t, 32, 8, 128,
+                            ctypes.c_float(1e-6), FAKE, 4096, None)
+    lib.dflash_kv_scatter(B.DFLASH_BF16, FAKE, FAKE, FAKE, t, 8, 128, FAKE, FAKE, 100000, None)
+    lib.dflash_context_kv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, t, 4096, 8, 128, ctypes.c_float(1e-6), FAKE,
+                          32768, FAKE, FAKE, FAKE, 1 << 40, None)
+    calls += 3
+os.environ["DFLASH_VALIDATE"] = "0"
 lib.dflash_rope_table(FAKE, 4096, 128, ctypes.c_double(1e6), None)
 # most random batches pass the checks and reach the planners and the launch
 assert codes.get(B.DFLASH_ERR_HIP, 0) + codes.get(B.DFLASH_OK, 0) > 800, codes

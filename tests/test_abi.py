@@ -7,6 +7,7 @@ import os
 import re
 import shutil
 import subprocess
+import sys
 
 import pytest
 
@@ -316,3 +317,29 @@ def test_noalloc_scratch_size_matches_header():
     text = open(HEADER).read()
     m = re.search(r"#define DFLASH_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
     assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+
+
+_NO_DEVICE_CHILD = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from block_diffusion_draft_dflash_amd import binding as B
+lib = B.load()
+fake = ctypes.c_void_p(1 << 40)  # valid-looking, aligned; never dereferenced on the host
+rc = lib.dflash_qk_norm_rope(B.DFLASH_BF16, fake, fake, fake, fake, fake, 16, 32, 8, 128,
+                             ctypes.c_float(1e-6), fake, 4096, None)
+print(rc, lib.dflash_last_error().decode())
+"""
+
+
+def test_launch_without_a_device_reports_a_hip_error():
+    # A call whose arguments pass every host check, made where the HIP runtime
+    # has no device: the launch fails and the call says so (DFLASH_ERR_HIP with
+    # the runtime's message) instead of crashing or reporting success.
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1", DFLASH_VALIDATE="0")
+    res = subprocess.run([sys.executable, "-c", _NO_DEVICE_CHILD, ROOT], env=env,
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rc, _, msg = res.stdout.strip().splitlines()[-1].partition(" ")
+    assert int(rc) == B.DFLASH_ERR_HIP, res.stdout
+    assert "HIP error" in msg, msg
