@@ -31,6 +31,9 @@
 //   second kernel merges each request's splits in split order, so the result
 //   is deterministic.
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <mutex>
 
 #include "dflash_device.h"
@@ -1378,6 +1381,50 @@ bool plan_block_attention(const dflash_block_attn_params& p, int num_cus, bool p
   return true;
 }
 
+namespace {
+
+// DFLASH_TRACE (environment variable, read at every call; anything but "" or
+// "0"): one host-side log of each attention call's work decomposition on
+// stderr: the split, the units per kv-head, the launch shapes, and per request
+// (host plan) its keys, splits and split size.
+bool trace_enabled() {
+  const char* v = std::getenv("DFLASH_TRACE");
+  return v && v[0] != '\0' && std::strcmp(v, "0") != 0;
+}
+
+void trace_plan(const dflash_block_attn_params& p, const AttnPlan& plan, const HostSched& hs,
+                bool paged, bool fused, int nstage, size_t lds, dim3 grid, dim3 mgrid) {
+  std::fprintf(stderr,
+               "dflash trace: block_attention %s%s: %d requests, Hq %d, Hkv %d, Dh %d, %lld context "
+               "rows, %lld block rows (max %d), causal %d, window %d\n",
+               paged ? "paged" : "packed", fused ? " + fused q/k norm and RoPE" : "", p.num_reqs,
+               p.num_q_heads, p.num_kv_heads, p.head_dim, (long long)p.total_ctx,
+               (long long)p.total_blk, p.max_blk_len, p.causal, p.window);
+  if (hs.nreq > 0)
+    std::fprintf(stderr, "  plan: host, split %d keys, %d units per kv-head (budget %lld), %d query tiles\n",
+                 hs.chunk, hs.nunits, (long long)plan.units, plan.qtiles);
+  else
+    std::fprintf(stderr,
+                 "  plan: on the device from the device lengths (split %s), budget %lld units per "
+                 "kv-head, %d query tiles\n",
+                 plan.chunk > 0 ? "fixed by split_keys" : "chosen by the kernels", (long long)plan.units,
+                 plan.qtiles);
+  std::fprintf(stderr,
+               "  launch: main grid (%u, %u, %u) x %d threads, %d LDS stages (%zu bytes); merge grid "
+               "%u x %d; workspace %zu bytes\n",
+               grid.x, grid.y, grid.z, NT, nstage, lds, mgrid.x, NT, plan.bytes);
+  for (int32_t r = 0; r < hs.nreq; ++r) {
+    const ReqSched& q = hs.req[r];
+    const int32_t qt = q.blen > 0 ? (plan.group * q.blen + QROWS - 1) / QROWS : 0;
+    std::fprintf(stderr,
+                 "  request %d: %d context + %d block rows, keys from %d, %d split(s) of up to %d "
+                 "keys x %d query tile(s)\n",
+                 r, q.clen, q.blen, q.lo, q.ns, q.csz, qt);
+  }
+}
+
+}  // namespace
+
 hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnPlan& plan,
                                   const dflash_qk_prologue* pro, const dflash_paged_ctx* pg,
                                   const int32_t* cu_ctx, const int32_t* cu_blk, const void* q,
@@ -1469,6 +1516,7 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   const dim3 grid((unsigned)p.num_kv_heads, (unsigned)std::min<int64_t>(launch_units, 65535),
                   (unsigned)((launch_units + 65534) / 65535));
   const dim3 blk(NT), mgrid((unsigned)mblocks);
+  if (trace_enabled()) trace_plan(p, plan, a.hs, pg != nullptr, pro != nullptr, nstage, lds, grid, mgrid);
   auto launch_main = [&](auto kernel) { hipLaunchKernelGGL(kernel, grid, blk, lds, s, a); };
   if (p.head_dim == 128) {
     if (nstage == 3) {

@@ -343,3 +343,40 @@ def test_launch_without_a_device_reports_a_hip_error():
     rc, _, msg = res.stdout.strip().splitlines()[-1].partition(" ")
     assert int(rc) == B.DFLASH_ERR_HIP, res.stdout
     assert "HIP error" in msg, msg
+
+
+_TRACE_CHILD = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from block_diffusion_draft_dflash_amd import binding as B
+lib = B.load()
+fake = ctypes.c_void_p(1 << 40)
+ctx, blk = [0, 700, 1900, 2400], [0, 16, 32, 48]
+p = B.make_block_attn_params(3, 32, 8, 128, B.DFLASH_BF16, 2400, 48, 16, 128 ** -0.5, False, 0, 0,
+                             host_cu_ctx_lens=ctx, host_cu_blk_lens=blk)
+ws = lib.dflash_block_attention_workspace_size(ctypes.byref(p))
+rc = lib.dflash_block_attention(ctypes.byref(p), None, fake, fake, fake, fake, fake, fake, fake, fake,
+                                fake, ws, None)
+print(rc, ws)
+"""
+
+
+def test_trace_mode_logs_the_work_split():
+    # DFLASH_TRACE prints each attention call's decomposition before the launch
+    # (here the launch itself then fails: no device is visible to the child)
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1", DFLASH_VALIDATE="0", DFLASH_TRACE="1")
+    res = subprocess.run([sys.executable, "-c", _TRACE_CHILD, ROOT], env=env, capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rc, ws = (int(x) for x in res.stdout.split()[-2:])
+    assert rc == B.DFLASH_ERR_HIP
+    log = res.stderr
+    assert "dflash trace: block_attention packed: 3 requests, Hq 32, Hkv 8, Dh 128" in log, log
+    assert "plan: host, split" in log and f"workspace {ws} bytes" in log, log
+    for r, (c, b) in enumerate([(700, 16), (1200, 16), (500, 16)]):
+        assert f"request {r}: {c} context + {b} block rows" in log, log
+    env["DFLASH_TRACE"] = "0"
+    quiet = subprocess.run([sys.executable, "-c", _TRACE_CHILD, ROOT], env=env, capture_output=True,
+                           text=True, timeout=300)
+    assert "dflash trace" not in quiet.stderr
