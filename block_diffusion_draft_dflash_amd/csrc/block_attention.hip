@@ -982,17 +982,55 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void
   pt_record(pt_rec, pt0, pt1, pt2, pt3, ntiles, 1);
 }
 
+// Streaming log-sum-exp over a row's ns split partials in index order, MB
+// splits per batch (their loads issued together): the row's running max M,
+// sum L and output o. Split s's record sits at ml_row[s * sstride] and its
+// values at ov_row[s * sstride * DH].
+template <int MB, int DV, int DH>
+__device__ __forceinline__ void merge_splits(const float4* ml_row, const f16* ov_row, int64_t sstride,
+                                             int32_t ns, float& M, float& L, float (&o)[DV]) {
+  for (int32_t s0 = 0; s0 < ns; s0 += MB) {
+    float4 ml[MB];
+    f16x8 ov[MB];
+#pragma unroll
+    for (int bb = 0; bb < MB; ++bb) {
+      const int64_t sidx = s0 + bb < ns ? s0 + bb : ns - 1;
+      ml[bb] = ml_row[sidx * sstride];
+      ov[bb] = *reinterpret_cast<const f16x8*>(ov_row + sidx * sstride * DH);
+    }
+    float bm = M;
+#pragma unroll
+    for (int bb = 0; bb < MB; ++bb)
+      if (s0 + bb < ns) bm = fmaxf(bm, ml[bb].x);
+    const float bsafe = (bm == -INFINITY) ? 0.f : bm;
+    const float rescale = fast_exp2(M - bsafe);
+    L *= rescale;
+#pragma unroll
+    for (int d = 0; d < DV; ++d) o[d] *= rescale;
+#pragma unroll
+    for (int bb = 0; bb < MB; ++bb) {
+      // split weight: its sum l times 2^(m - M); its values are O / l stored
+      // times 2^-e
+      const float wgt = (s0 + bb < ns) ? ml[bb].y * fast_exp2(ml[bb].x - bsafe) : 0.f;
+      const float wov = ldexpf(wgt, (int)ml[bb].z);
+      L += wgt;
+#pragma unroll
+      for (int d = 0; d < DV; ++d) o[d] += (float)ov[bb][d] * wov;
+    }
+    M = bm;
+  }
+}
+
 // Merge of split partials: one workgroup per (request, query tile, kv-head,
 // block of MROWS rows); thread -> (row, 8 head-dim values). Splits are
 // consumed in index order by a streaming log-sum-exp, MB at a time with their
 // loads in flight, so the result does not depend on scheduling.
 constexpr int MROWS = 16;
 template <int DH>
-__global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(1, 2))) void block_attn_merge_kernel(AttnArgs a) {
   constexpr int DV = 8;                   // head-dim values per thread
   constexpr int TPR = DH / DV;            // threads per row
   constexpr int RPW = NT / TPR;           // rows per workgroup pass
-  constexpr int MB = 8;
   const int32_t rb_count = QROWS / MROWS;
   const uint64_t pt0 = pt_now();
   // What the host-planned path needs is read before any branch: the scalar
@@ -1047,37 +1085,16 @@ __global__ __launch_bounds__(NT) void block_attn_merge_kernel(AttnArgs a) {
 #pragma unroll
     for (int d = 0; d < DV; ++d) o[d] = 0.f;
     float M = -INFINITY, L = 0.f;
-    for (int32_t s0 = 0; s0 < ns; s0 += MB) {
-      float4 ml[MB];
-      f16x8 ov[MB];
-#pragma unroll
-      for (int bb = 0; bb < MB; ++bb) {
-        const int32_t sidx = s0 + bb < ns ? s0 + bb : ns - 1;
-        const int64_t slot = (int64_t)(first + sidx) * a.hkv + g;
-        ml[bb] = pml[slot * QROWS + row];
-        ov[bb] = *reinterpret_cast<const f16x8*>(a.part_o + (slot * QROWS + row) * DH + d0);
-      }
-      float bm = M;
-#pragma unroll
-      for (int bb = 0; bb < MB; ++bb)
-        if (s0 + bb < ns) bm = fmaxf(bm, ml[bb].x);
-      const float bsafe = (bm == -INFINITY) ? 0.f : bm;
-      const float rescale = fast_exp2(M - bsafe);
-      L *= rescale;
-#pragma unroll
-      for (int d = 0; d < DV; ++d) o[d] *= rescale;
-#pragma unroll
-      for (int bb = 0; bb < MB; ++bb) {
-        // split weight: its sum l times 2^(m - M); its values are O / l
-        // stored times 2^-e
-        const float wgt = (s0 + bb < ns) ? ml[bb].y * fast_exp2(ml[bb].x - bsafe) : 0.f;
-        const float wov = ldexpf(wgt, (int)ml[bb].z);
-        L += wgt;
-#pragma unroll
-        for (int d = 0; d < DV; ++d) o[d] += (float)ov[bb][d] * wov;
-      }
-      M = bm;
-    }
+    // The splits in batches of MB whose loads are in flight together: MB = 8
+    // up to 8 splits, else 16 (one memory round trip for up to 16 splits at
+    // the cost of more registers). The batch size depends on the split count
+    // only, so every plan that splits a request the same way gives the same
+    // bits.
+    const float4* ml_row = pml + (int64_t)first * a.hkv * QROWS + (int64_t)g * QROWS + row;
+    const f16* ov_row = a.part_o + ((int64_t)first * a.hkv * QROWS + (int64_t)g * QROWS + row) * DH + d0;
+    const int64_t sstride = (int64_t)a.hkv * QROWS;  // between consecutive splits, in rows
+    if (ns <= 8) merge_splits<8, DV, DH>(ml_row, ov_row, sstride, ns, M, L, o);
+    else merge_splits<16, DV, DH>(ml_row, ov_row, sstride, ns, M, L, o);
     if (nq2 < nrows) {
       const int32_t hl2 = nq2 / blen;
       const int32_t b2 = nq2 - hl2 * blen;
