@@ -19,8 +19,11 @@
 // k-slices of A and B are copied HBM -> LDS directly (no register staging),
 // the next slice in flight while the current one is consumed, with explicit
 // waits and one fence-free barrier per slice; each wave's fragment reads are
-// interleaved with its MFMAs. The epilogue stages each wave's bf16 tile in
-// LDS and writes whole 16-byte pieces of the output rows.
+// interleaved with its MFMAs. The products are formed transposed (weights as
+// the first operand), so each lane ends up with four consecutive columns of
+// its rows: the epilogue completes a row's k-norm with one cross-lane add,
+// reads the rows' cos/sin from LDS (copied there once per tile) and stores
+// 8-byte pieces of the output rows straight from registers.
 #include <mutex>
 
 #include "dflash_device.h"
@@ -97,25 +100,10 @@ __device__ __forceinline__ void block_barrier() {
 
 constexpr int NTG = 256;  // GEMM workgroup: 4 waves, one per SIMD
 
-// Sum over the 32 lanes of each half of the wave with DPP swaps (quad xor 1,
-// quad xor 2, half-row and row mirrors) and one 16-lane row swap.
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-__device__ __forceinline__ float lane32_sum(float v) {
-  v += dpp_f<0xB1>(v);   // quad_perm [1, 0, 3, 2]
-  v += dpp_f<0x4E>(v);   // quad_perm [2, 3, 0, 1]
-  v += dpp_f<0x141>(v);  // row_half_mirror
-  v += dpp_f<0x140>(v);  // row_mirror
-  const int x = __float_as_int(v);
-  auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-  return __int_as_float(b[0]) + __int_as_float(b[1]);
-}
-
 // One workgroup computes a 256-row x 256-column tile (two heads) of
 // [K | V] = h W'^T over the whole of H. Wave w owns rows 128 (w & 1) ..+127
-// and head (w >> 1) of the tile: 4 x 4 blocks of 32 x 32 outputs on
+// and head (w >> 1) of the tile: 4 x 4 blocks of 32 x 32 outputs (formed as
+// W' h^T, so that a lane holds row elements) on
 // v_mfma_f32_32x32x16_bf16, whose 256 f32 accumulators per lane sit in the
 // accumulation registers. (With one wave per SIMD the 32x32 form keeps the
 // matrix pipe busy back to back; measured on this GPU, the 16x16x32 form
@@ -236,8 +224,12 @@ __device__ __forceinline__ void ctx_kv_gemm_body(const CkvArgs& a, bf16* smem) {
     if (q < 8) nb[q] = frag(st_idx, b_lane[jj][q >> 2], q & 3);
     else na[q - 8] = frag(st_idx, a_lane[jj][(q - 8) >> 2], (q - 8) & 3);
   };
+  // The weight block goes in as the first operand and the hidden block as the
+  // second, so that the accumulators come out transposed: lane (l32, hi)
+  // holds row 32 x + l32 of block (x, y) at the four consecutive columns
+  // 32 y + 8 q + 4 hi .. +3 for q = e / 4 (see the epilogue).
   auto mma = [&](const bf16x8 (&ca)[8], const bf16x8 (&cb)[8], int x, int h, int y) {
-    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ca[4 * h + x], cb[4 * h + y], acc[x][y],
+    acc[x][y] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cb[4 * h + y], ca[4 * h + x], acc[x][y],
                                                         0, 0, 0);
   };
   // The 32 MFMAs of one sub-slice on (ca, cb), with the 16 fragment reads of
@@ -282,6 +274,12 @@ __device__ __forceinline__ void ctx_kv_gemm_body(const CkvArgs& a, bf16* smem) {
       }
   };
 
+  // K tiles: the positions of the tile's rows (thread t: row t), loaded ahead
+  // of the slices so that the epilogue does not wait for them.
+  const bool is_k = col0 < a.hkv * DH;  // a 256-column tile is all K or all V
+  int32_t my_pos = 0;
+  if (is_k) my_pos = a.pos[min(row0 + tid, a.rows - 1)];
+
   bf16x8 fa[8], fb[8], ga[8], gb[8];
   issue(0);
   if (nst > 1) {
@@ -307,18 +305,31 @@ __device__ __forceinline__ void ctx_kv_gemm_body(const CkvArgs& a, bf16* smem) {
   core(fa, fb, ga, gb, nst - 1, 1);  // the last stage
   core_last(ga, gb);
 
-  // Row scale of the hidden RMSNorm, 1 / sqrt(mean(h^2) + eps): the two
-  // waves' partial sums of each row meet in LDS (after the transposition area
-  // of the epilogue), with the rows' positions (K tiles).
-  float* rpart = reinterpret_cast<float*>(smem + NW * 128 * 128);  // [2][256]
-  float* rsc = rpart + 512;                                       // [256] row scales
-  int32_t* rpos = reinterpret_cast<int32_t*>(rsc + 256);          // [256] clamped positions
+  // Epilogue. After the slices the LDS holds, from its start: the cos/sin
+  // rows of the tile's 256 rows (K tiles; row t at t * CS_STRIDE bytes), then
+  // the two waves' partial row sums, the row scales and the clamped positions.
+  // The cos/sin rows are 16 bytes further apart than their 512 bytes, so that
+  // the 32 lanes reading one offset of 32 consecutive rows hit distinct banks.
+  constexpr int CS_STRIDE = HALF * 8 + 16;
+  char* const lds_b = reinterpret_cast<char*>(smem);
+  float* rpart = reinterpret_cast<float*>(lds_b + 256 * CS_STRIDE);  // [2][256]
+  float* rsc = rpart + 512;                                          // [256] row scales
+  int32_t* rpos = reinterpret_cast<int32_t*>(rsc + 256);             // [256] clamped positions
   const int head = (col0 + DH * wn) / DH;  // 0..2*Hkv-1: K heads first, then V heads
-  const bool is_k = col0 < a.hkv * DH;     // a 256-column tile is all K or all V
-  int32_t my_pos = 0;
-  if (is_k) my_pos = a.pos[min(row0 + tid, a.rows - 1)];
+  const int hh = is_k ? head : head - a.hkv;
+  bf16* dst_base = is_k ? a.k_out : a.v_out;
+  // the k-norm weights of this lane's columns 32 y + 8 q + 4 hi .. +3
+  float4 kwv[4][4];
+  if (is_k) {
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) kwv[y][q] = *reinterpret_cast<const float4*>(a.knw + 32 * y + 8 * q + 4 * hi);
+  }
   wait_lgkm0();
   block_barrier();  // every wave is done with the stages
+  // Row scale of the hidden RMSNorm, 1 / sqrt(mean(h^2) + eps): the two
+  // waves' partial sums of each row meet in LDS, with the rows' positions.
 #pragma unroll
   for (int x = 0; x < 4; ++x) {
     const float ss = hsq[x][0] + hsq[x][1];
@@ -328,95 +339,81 @@ __device__ __forceinline__ void ctx_kv_gemm_body(const CkvArgs& a, bf16* smem) {
   rpos[tid] = my_pos < 0 ? 0 : (my_pos >= a.max_pos ? a.max_pos - 1 : my_pos);
   wait_lgkm0();
   block_barrier();
-  rsc[tid] = 1.0f / sqrtf((rpart[tid] + rpart[256 + tid]) / (float)a.hidden + a.eps);
-  wait_lgkm0();
-  block_barrier();
-
-  // Epilogue. acc[x][y][e] = C[row0 + 128 wm + 32 x + 8 (e / 4) + 4 hi + e % 4]
-  //                           [col0 + 128 wn + 32 y + l32]:
-  // this wave holds one whole head of its 128 rows, so the k-norm's sums and
-  // the rotate-half pairs (d, d + 64) = blocks (y, y + 2) stay in the wave.
-  bf16* dst_base = is_k ? a.k_out : a.v_out;
-  const int hh = is_k ? head : head - a.hkv;
-  // The wave's bf16 tile goes through LDS ([128 rows][128 cols], 16-byte
-  // chunk q of row r at q ^ (r & 15)) so that the stores are whole 16-byte
-  // pieces of each 256-byte output row.
-  bf16* tl = smem + w * 128 * 128;
-  auto rloc_of = [&](int x, int e) { return 32 * x + 8 * (e >> 2) + 4 * hi + (e & 3); };
-  auto store_lds = [&](int rloc, const float (&v)[4]) {
-#pragma unroll
-    for (int y = 0; y < 4; ++y) {
-      const int col = 32 * y + l32;
-      tl[rloc * 128 + (((col >> 3) ^ (rloc & 15)) << 3) + (col & 7)] = f2bf(v[y]);
-    }
-  };
   if (is_k) {
-    float kw[4];
-#pragma unroll
-    for (int y = 0; y < 4; ++y) kw[y] = a.knw[32 * y + l32];
-    // cos/sin of the lane's pairs (d = 32 y + l32, y < 2) for 8 rows at a
-    // time (half of block x), fetched one group ahead
-    float2 cs[2][8][2];
-    auto fetch = [&](int g, float2 (&c)[8][2]) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = 8 * (g & 1) + i;
-        const float2* t = a.table + (int64_t)rpos[128 * wm + rloc_of(g >> 1, e)] * HALF + l32;
-        c[i][0] = t[0];
-        c[i][1] = t[32];
-      }
-    };
-    fetch(0, cs[0]);
-#pragma unroll
-    for (int g = 0; g < 8; ++g) {
-      if (g + 1 < 8) fetch(g + 1, cs[(g + 1) & 1]);
-      const int x = g >> 1;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        const int e = 8 * (g & 1) + i;
-        const int rloc = rloc_of(x, e);
-        const float rs = rsc[128 * wm + rloc];
-        float v[4];
-        float ss = 0.f;
-#pragma unroll
-        for (int y = 0; y < 4; ++y) {
-          v[y] = acc[x][y][e] * rs;
-          ss += v[y] * v[y];
-        }
-        ss = lane32_sum(ss);  // the 32 lanes of this half hold the row's 128 columns
-        const float inv = 1.0f / sqrtf(ss * (1.0f / DH) + a.eps);
-#pragma unroll
-        for (int y = 0; y < 2; ++y) {  // pairs (d, d + 64): blocks y and y + 2
-          const float2 c = cs[g & 1][i][y];
-          const float lo = v[y] * inv * kw[y], hi2 = v[y + 2] * inv * kw[y + 2];
-          v[y] = lo * c.x - hi2 * c.y;
-          v[y + 2] = hi2 * c.x + lo * c.y;
-        }
-        store_lds(rloc, v);
+    // the cos/sin row of each of the tile's rows, HBM -> LDS: one 512-byte
+    // copy per row (32 lanes of 16 bytes), wave w taking rows 64 w .. 64 w + 63
+    for (int i = 0; i < 64; ++i) {
+      const int r = 64 * w + i;
+      const uint32_t dst = lds0 + (uint32_t)(r * CS_STRIDE);
+      if (lane < 32) {
+        const float2* src = a.table + (int64_t)rpos[r] * HALF + 2 * lane;
+        asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(dst), "v"(src)
+                     : "memory", "m0");
       }
     }
-  } else {
-#pragma unroll
-    for (int x = 0; x < 4; ++x)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int rloc = rloc_of(x, e);
-        const float rs = rsc[128 * wm + rloc];
-        float v[4];
-#pragma unroll
-        for (int y = 0; y < 4; ++y) v[y] = acc[x][y][e] * rs;
-        store_lds(rloc, v);
-      }
   }
-  wait_lgkm0();  // the wave reads back only its own tile
-#pragma unroll 4
-  for (int it = 0; it < 32; ++it) {
-    const int rloc = it * 4 + (lane >> 4);
-    const int q = lane & 15;
-    const int64_t row = row0 + 128 * wm + rloc;
-    const bf16x8 v = *reinterpret_cast<const bf16x8*>(tl + rloc * 128 + ((q ^ (rloc & 15)) << 3));
-    if (row < a.rows)
-      *reinterpret_cast<bf16x8*>(dst_base + (row * a.hkv + hh) * DH + q * 8) = v;
+  rsc[tid] = 1.0f / sqrtf((rpart[tid] + rpart[256 + tid]) / (float)a.hidden + a.eps);
+  wait_vmcnt<0>();  // this wave's cos/sin copies (and the weights) landed
+  wait_lgkm0();
+  block_barrier();  // every wave's copies and row scales are visible
+
+  // acc[x][y][e] = C[row0 + 128 wm + 32 x + l32][col0 + 128 wn + 32 y + 8 (e / 4) + 4 hi + e % 4]:
+  // each lane holds 64 of a row's 128 columns of this head (the other 64 in
+  // lane l ^ 32), the rotate-half pairs (d, d + 64) = blocks (y, y + 2) in
+  // the same lane, and writes whole 8-byte pieces of the output row.
+#pragma unroll
+  for (int x = 0; x < 4; ++x) {
+    const int rt = 128 * wm + 32 * x + l32;  // row within the tile
+    const int64_t row = row0 + rt;
+    const float rs = rsc[rt];
+    float v[4][16];
+#pragma unroll
+    for (int y = 0; y < 4; ++y)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) v[y][e] = acc[x][y][e] * rs;
+    if (is_k) {
+      float ss = 0.f;
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ss += v[y][e] * v[y][e];
+      ss += __shfl_xor(ss, 32, 64);  // the row's other 64 columns
+      const float inv = 1.0f / sqrtf(ss * (1.0f / DH) + a.eps);
+      const char* csrow = lds_b + rt * CS_STRIDE;
+#pragma unroll
+      for (int y = 0; y < 2; ++y)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          // cos/sin of dims d = 32 y + 8 q + 4 hi .. +3 (pairs (d, d + 64))
+          const f32x4 c01 = *reinterpret_cast<const f32x4*>(csrow + (32 * y + 8 * q + 4 * hi) * 8);
+          const f32x4 c23 = *reinterpret_cast<const f32x4*>(csrow + (32 * y + 8 * q + 4 * hi) * 8 + 16);
+          const float cs[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+          const float4 w0 = kwv[y][q], w1 = kwv[y + 2][q];
+          const float wlo[4] = {w0.x, w0.y, w0.z, w0.w}, whi[4] = {w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const int e = 4 * q + r4;
+            const float lo = v[y][e] * inv * wlo[r4], hi2 = v[y + 2][e] * inv * whi[r4];
+            const float c = cs[2 * r4], sn = cs[2 * r4 + 1];
+            v[y][e] = lo * c - hi2 * sn;
+            v[y + 2][e] = hi2 * c + lo * sn;
+          }
+        }
+    }
+    if (row < a.rows) {
+      bf16* drow = dst_base + (row * a.hkv + hh) * DH + 4 * hi;
+#pragma unroll
+      for (int y = 0; y < 4; ++y)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          bf16x4 o;
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) o[r4] = f2bf(v[y][4 * q + r4]);
+          *reinterpret_cast<bf16x4*>(drow + 32 * y + 8 * q) = o;
+        }
+    }
   }
 }
 
@@ -427,12 +424,13 @@ void ctx_kv_gemm_kernel(CkvArgs a) {
   else ctx_kv_gemm_body<1>(a, smem);
 }
 
-// LDS of the GEMM: the k-slice stages, or in the epilogue the four waves'
-// 128 x 128 bf16 tiles, the partial row sums, row scales and positions,
+// LDS of the GEMM: the k-slice stages, or in the epilogue the cos/sin rows
+// of the tile's rows, the partial row sums, row scales and positions,
 // whichever is larger.
-constexpr size_t kGemmLds = (size_t)NSTAGE * 2 * BM * BK * sizeof(bf16) > (size_t)4 * 128 * 128 * 2 + 4096
+constexpr size_t kEpiLds = (size_t)256 * (64 * 8 + 16) + 4096;
+constexpr size_t kGemmLds = (size_t)NSTAGE * 2 * BM * BK * sizeof(bf16) > kEpiLds
                                 ? (size_t)NSTAGE * 2 * BM * BK * sizeof(bf16)
-                                : (size_t)4 * 128 * 128 * 2 + 4096;
+                                : kEpiLds;
 
 }  // namespace
 
