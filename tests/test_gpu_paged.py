@@ -154,3 +154,16 @@ def test_paged_vs_oracle_through_the_pools(case):
     err = np.abs(to_host_f64(dp.out) - ref)
     print(f"[paged oracle {case}] max abs {err.max():.3e} mean abs {err.mean():.3e}")
     assert err.max() <= 2e-2 and err.mean() <= 2e-3
+    # and independently of the pools: the oracle's own context rows (its norm
+    # + RoPE of the raw keys, the raw values) against what the pools hold
+    # through the block table, and the attention on the oracle's rows
+    _, k_own = O.qk_norm_rope(None, wl.k_ctx, None, wl.k_norm_w, wl.ctx_positions, wl.eps, wl.theta)
+    bad = np.abs(k_ctx - k_own) > 2.0 ** -7 * np.abs(k_own) + 1e-5
+    assert not bad.any(), f"{bad.sum()} pooled K elements beyond one rounding of the oracle's"
+    assert np.array_equal(v_ctx, np.asarray(wl.v_ctx, dtype=np.float64)), "pooled V differs from the input"
+    ref_own, _, _ = O.draft_block_attention(wl.q, wl.k_blk, wl.v_blk, wl.blk_positions, k_own,
+                                            wl.v_ctx, wl.cu_ctx, wl.cu_blk, wl.q_norm_w, wl.k_norm_w,
+                                            wl.eps, wl.theta, wl.scale, wl.causal, wl.window)
+    err = np.abs(to_host_f64(dp.out) - ref_own)
+    print(f"[paged oracle {case}, oracle's own context rows] max abs {err.max():.3e} mean abs {err.mean():.3e}")
+    assert err.max() <= 2e-2 and err.mean() <= 2e-3
