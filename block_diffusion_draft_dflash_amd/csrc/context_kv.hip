@@ -105,9 +105,10 @@ constexpr int NTG = 256;  // GEMM workgroup: 4 waves, one per SIMD
 // and head (w >> 1) of the tile: 4 x 4 blocks of 32 x 32 outputs (formed as
 // W' h^T, so that a lane holds row elements) on
 // v_mfma_f32_32x32x16_bf16, whose 256 f32 accumulators per lane sit in the
-// accumulation registers. (With one wave per SIMD the 32x32 form keeps the
-// matrix pipe busy back to back; measured on this GPU, the 16x16x32 form
-// reaches ~1.4 PFLOP/s from one wave per SIMD against ~2.2 for 32x32x16.)
+// accumulation registers. (Back to back on register operands the 32x32x16
+// and 16x16x32 forms run within 5% of each other on this GPU, ~1.8-1.9
+// PFLOP/s on random data and ~2.2-2.3 on zeros; the 32x32 form needs 16
+// independent accumulators per wave where the 16x16 one needs 64.)
 // Each 64-k stage is consumed as two 32-k sub-slices: per sub-slice a wave
 // reads 8 A and 8 B fragments from LDS (16 KB) for 32 MFMAs, the next
 // sub-slice's fragments being read, and the current A fragments' squares
