@@ -184,11 +184,6 @@ __device__ __forceinline__ int32_t req_split_size(const LaneReq& q, int32_t ns) 
   return ns > 0 ? ((q.n + ns - 1) / ns + KT - 1) / KT * KT : 0;
 }
 
-__device__ __forceinline__ int32_t wave_sum(int32_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
-  return v;
-}
 __device__ __forceinline__ int64_t wave_sum64(int64_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
