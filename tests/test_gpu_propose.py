@@ -284,6 +284,19 @@ def test_context_kv_few_rows_vs_oracle(rows, hkv, h):
     # calls of fewer than 256 rows (a step's appended rows) take the
     # projection-GEMM path (K and V in one product over the two weights);
     # scale-relative bound as for the large-row form
+    _context_kv_vs_oracle(rows, hkv, h)
+
+
+# the large-row form (256 rows and more: the fused MFMA GEMM) at hidden sizes
+# of one, two and three 64-wide k-slices and up, whole and partial 256-row
+# tiles, and K / V head counts of 2 to 8 (two heads per 256-column tile)
+@pytest.mark.parametrize("rows,hkv,h", [(256, 2, 64), (300, 2, 128), (520, 4, 192), (777, 8, 1024),
+                                        (1030, 2, 64)])
+def test_context_kv_large_rows_shapes_vs_oracle(rows, hkv, h):
+    _context_kv_vs_oracle(rows, hkv, h)
+
+
+def _context_kv_vs_oracle(rows, hkv, h):
     from oracle import dflash_oracle as O
     print(f"case context_kv rows={rows} hkv={hkv} h={h}", flush=True)
     rng = np.random.default_rng(rows)
@@ -312,9 +325,12 @@ def test_context_kv_few_rows_vs_oracle(rows, hkv, h):
         print(f"[context_kv rows={rows} {name}] scale-relative max err {rel:.3e}", flush=True)
         assert rel <= 1e-2
     if rows > 1:
-        # row independence within this form: two calls over row chunks
+        # row independence within this form: calls over row chunks of the same
+        # form (fewer than 256 rows, else 256-row windows at both ends; the
+        # two forms add in different orders)
         cut = rows // 3
-        for lo, hi in ((0, cut), (cut, rows)):
+        chunks = ((0, cut), (cut, rows)) if rows < 256 else ((0, 256), (rows - 256, rows))
+        for lo, hi in chunks:
             kc = torch.empty((hi - lo, hkv, dh), dtype=torch.bfloat16, device=dev)
             vc = torch.empty_like(kc)
             B.dflash_context_kv(*args(lo, hi, kc, vc))
