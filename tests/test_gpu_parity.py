@@ -170,6 +170,11 @@ EDGE = {
     "window1": dict(name="swa", num_reqs=2, ctx_len=100, window=1),
     "window_gt_len": dict(name="swa", num_reqs=2, ctx_len=100, window=5000),
     "causal_long_block": dict(name="swa", ctx_lens=[40, 0], blk_lens=[70, 33], window=50),
+    # blocks far longer than a key tile and a query tile: 300 rows x G 4 = 19
+    # query tiles, the last one partial; bidirectional, then causal with a
+    # window shorter than the block
+    "long_blocks": dict(name="qwen3_8b_draft", ctx_lens=[100, 0, 37], blk_lens=[300, 129, 1]),
+    "long_blocks_window": dict(name="swa", ctx_lens=[500, 20], blk_lens=[257, 100], window=128),
     "f32_varlen": dict(name="tiny", ctx_lens=[0, 64, 129], blk_lens=[16, 5, 0], hq=8, hkv=2, dh=128),
     "f32_causal": dict(name="tiny", ctx_lens=[64, 10], blk_lens=[16, 16], causal=True, window=20),
 }
@@ -185,7 +190,7 @@ def test_parity_edges(case):
 
 
 @pytest.mark.parametrize("case", ["empty_ctx_and_blocks", "dh64_bf16", "causal_long_block",
-                                  "window1", "mqa", "gqa16"])
+                                  "window1", "mqa", "gqa16", "long_blocks", "long_blocks_window"])
 def test_parity_edges_device_planned(case):
     # the work split derived by the kernels from the device lengths alone
     print(f"case edge device-planned {case}", flush=True)
