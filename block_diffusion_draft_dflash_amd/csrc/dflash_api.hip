@@ -440,10 +440,15 @@ dflash_status dflash_kv_scatter(dflash_dtype dtype, const void* k_src, const voi
 // Calls with fewer rows than one tile of the large-row kernel (a propose
 // step appending its verified rows) take the projection-GEMM path.
 constexpr int64_t kCtxKvRowsPath = 256;
+// Upper bound on the context projection's output width (Hkv * Dh) and on its
+// hidden size: keeps every product of the two in the planners inside 32 bits.
+constexpr int32_t kMaxProjDim = 1 << 20;
 
 size_t dflash_context_kv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_kv_heads,
                                         int32_t head_dim) {
   if (T < 0 || hidden_size < 1 || num_kv_heads < 1 || head_dim < 1) return 0;
+  // sizes the call itself rejects (and whose products would not fit 32 bits)
+  if ((int64_t)num_kv_heads * head_dim > kMaxProjDim || hidden_size > kMaxProjDim) return 0;
   if (T < kCtxKvRowsPath)
     return dflash::context_kv_rows_workspace_bytes(T, hidden_size, num_kv_heads, head_dim,
                                                    kPlanComputeUnits);
@@ -460,8 +465,11 @@ dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, 
   if (num_kv_heads < 1) return fail(DFLASH_ERR_INVALID_ARG, "context_kv: num_kv_heads must be >= 1");
   if (head_dim != 128)
     return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: head_dim %d is not supported (128)", head_dim);
-  if (hidden_size < 64 || hidden_size % 64 != 0)
-    return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: hidden_size must be a positive multiple of 64");
+  if ((int64_t)num_kv_heads * head_dim > kMaxProjDim)
+    return fail(DFLASH_ERR_INVALID_ARG, "context_kv: num_kv_heads * head_dim must be <= %d", kMaxProjDim);
+  if (hidden_size < 64 || hidden_size % 64 != 0 || hidden_size > kMaxProjDim)
+    return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: hidden_size must be a multiple of 64 in [64, %d]",
+                kMaxProjDim);
   if ((num_kv_heads * head_dim) % 256 != 0)
     return fail(DFLASH_ERR_UNSUPPORTED, "context_kv: num_kv_heads * head_dim must be a multiple of 256");
   if (!(eps >= 0.f) || !std::isfinite(eps))
@@ -506,7 +514,11 @@ dflash_status dflash_context_kv(const void* hidden, const float* hidden_norm_w, 
 
 size_t dflash_block_qkv_workspace_size(int64_t T, int32_t hidden_size, int32_t num_q_heads,
                                        int32_t num_kv_heads, int32_t head_dim) {
-  if (T < 0 || hidden_size < 64 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1) return 0;
+  if (T < 0 || T > INT32_MAX || hidden_size < 64 || num_q_heads < 1 || num_kv_heads < 1 || head_dim < 1)
+    return 0;
+  if (((int64_t)num_q_heads + 2 * (int64_t)num_kv_heads) * head_dim > INT32_MAX / 2 ||
+      hidden_size > kMaxProjDim)
+    return 0;  // rejected by the call
   return dflash::block_qkv_workspace_bytes(T, hidden_size, num_q_heads, num_kv_heads, head_dim,
                                            kPlanComputeUnits);
 }
@@ -523,7 +535,7 @@ dflash_status dflash_block_qkv(const void* hidden, void* residual, const float* 
     return fail(DFLASH_ERR_UNSUPPORTED, "block_qkv: head_dim %d is not supported (64 or 128)", head_dim);
   if (hidden_size < 64 || hidden_size % 64 != 0 || hidden_size > 8192)
     return fail(DFLASH_ERR_UNSUPPORTED, "block_qkv: hidden_size must be a multiple of 64 in [64, 8192]");
-  if ((int64_t)(num_q_heads + 2 * num_kv_heads) * head_dim > INT32_MAX / 2)
+  if (((int64_t)num_q_heads + 2 * (int64_t)num_kv_heads) * head_dim > INT32_MAX / 2)
     return fail(DFLASH_ERR_INVALID_ARG, "block_qkv: too many heads");
   if (!(eps >= 0.f) || !std::isfinite(eps))
     return fail(DFLASH_ERR_INVALID_ARG, "block_qkv: eps must be finite and >= 0");
@@ -547,7 +559,7 @@ dflash_status dflash_block_qkv(const void* hidden, void* residual, const float* 
 }
 
 size_t dflash_o_proj_workspace_size(int64_t T, int32_t hidden_size, int32_t in_dim) {
-  if (T < 0 || hidden_size < 64 || in_dim < 64) return 0;
+  if (T < 0 || T > INT32_MAX || hidden_size < 64 || in_dim < 64) return 0;
   return dflash::o_proj_workspace_bytes(T, hidden_size, in_dim, kPlanComputeUnits);
 }
 
@@ -611,7 +623,8 @@ dflash_status dflash_prepare_inputs(const dflash_prepare_params* p,
 }
 
 size_t dflash_fc_combine_workspace_size(int64_t T, int32_t hidden_size, int32_t num_taps) {
-  if (T < 0 || hidden_size < 64 || num_taps < 1) return 0;
+  if (T < 0 || T > INT32_MAX || hidden_size < 64 || num_taps < 1) return 0;
+  if ((int64_t)hidden_size * num_taps > INT32_MAX / 2) return 0;  // rejected by the call
   return dflash::fc_combine_workspace_bytes(T, hidden_size, num_taps, kPlanComputeUnits);
 }
 

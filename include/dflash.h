@@ -334,7 +334,8 @@ dflash_status dflash_kv_scatter(dflash_dtype dtype, const void* k_src, const voi
  *   k_out, v_out  bf16 [T, Hkv, Dh], written
  *   workspace     device, 256-byte aligned, >= dflash_context_kv_workspace_size
  *                 bytes (no zero-fill needed)
- * Requirements: Dh == 128, H % 64 == 0, (Hkv * Dh) % 256 == 0. Calls of at
+ * Requirements: Dh == 128, H % 64 == 0, (Hkv * Dh) % 256 == 0, H and Hkv * Dh
+ * at most 2^20 (the workspace-size query returns 0 beyond). Calls of at
  * least 256 rows fold the norm weight into the weights and run one fused
  * GEMM + k-norm + RoPE kernel; calls of fewer rows (a propose step appending
  * its verified rows) round the normed rows to bf16, run the split-K projection

@@ -123,6 +123,22 @@ for t, h in itertools.product([0, 1, 5, 128, 255, 256, 1000, 4096], [64, 512, 40
                             ctypes.c_float(1e-6), FAKE, 4096, None)
     lib.dflash_kv_scatter(B.DFLASH_BF16, FAKE, FAKE, FAKE, t, 8, 128, FAKE, FAKE, 100000, None)
     calls += 10
+# sizes whose products would not fit 32 bits: every query returns 0 and every
+# call an error status, with no overflow on the way
+big = 1 << 30
+for t in (1, 300, 1 << 40):
+    assert lib.dflash_context_kv_workspace_size(t, 4096, big, 128) == 0
+    assert lib.dflash_context_kv_workspace_size(t, big, 8, 128) == 0
+    assert lib.dflash_block_qkv_workspace_size(t, 4096, big, big, 128) == 0
+    assert lib.dflash_fc_combine_workspace_size(t, 4096, big) == 0
+    for h, hkv in ((4096, big), (4096, 1 << 24), (big, 8)):
+        assert lib.dflash_context_kv(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, t, h, hkv, 128, ctypes.c_float(1e-6),
+                                     FAKE, 32768, FAKE, FAKE, FAKE, 1 << 40, None) < 0
+    assert lib.dflash_block_qkv(FAKE, FAKE, FAKE, FAKE, t, 4096, big, big, 128, ctypes.c_float(1e-6), FAKE,
+                                FAKE, FAKE, FAKE, 1 << 40, None) < 0
+    assert lib.dflash_fc_combine(FAKE, FAKE, t, 4096, big, FAKE, FAKE, 1 << 40, None) < 0
+    calls += 6
+assert lib.dflash_o_proj_workspace_size(1 << 40, 4096, 4096) == 0
 os.environ["DFLASH_VALIDATE"] = "1"
 for t in (1, 300):
     lib.dflash_qk_norm_rope(B.DFLASH_BF16, FAKE, FAKE, FAKE, FAKE, FAKE, t, 32, 8, 128,
