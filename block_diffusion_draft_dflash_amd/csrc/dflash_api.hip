@@ -190,7 +190,8 @@ dflash_status dflash_block_attention_check(const dflash_block_attn_params* p) {
   if (st != DFLASH_OK) return st;
   if (p->total_ctx < 0 || p->total_blk < 0)
     return fail(DFLASH_ERR_INVALID_ARG, "block_attention: total_ctx/total_blk must be >= 0");
-  if (p->total_ctx + p->total_blk > INT32_MAX / 2)
+  if (p->total_ctx > INT32_MAX / 2 || p->total_blk > INT32_MAX / 2 ||
+      p->total_ctx + p->total_blk > INT32_MAX / 2)
     return fail(DFLASH_ERR_INVALID_ARG, "block_attention: total rows must be < 2^30");
   if (p->max_blk_len < 0 || p->max_blk_len > p->total_blk)
     return fail(DFLASH_ERR_INVALID_ARG, "block_attention: max_blk_len must be in [0, total_blk]");

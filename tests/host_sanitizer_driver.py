@@ -65,7 +65,8 @@ for kw in [dict(), dict(num_reqs=0), dict(num_q_heads=30), dict(num_kv_heads=0),
            dict(head_dim=64), dict(dtype=B.DFLASH_F32), dict(dtype=7), dict(total_ctx=-1),
            dict(max_blk_len=200), dict(max_blk_len=0), dict(window=64), dict(window=64, causal=True),
            dict(split_keys=100), dict(split_keys=64), dict(split_keys=1 << 24),
-           dict(total_ctx=2 ** 30), dict(total_ctx=0), dict(total_blk=0, max_blk_len=0),
+           dict(total_ctx=2 ** 30), dict(total_ctx=2 ** 62, total_blk=2 ** 62), dict(total_ctx=0),
+           dict(total_blk=0, max_blk_len=0), dict(num_q_heads=2 ** 31 - 1, num_kv_heads=1),
            dict(num_reqs=70000, total_ctx=70000 * 10, total_blk=70000 * 16),
            dict(num_q_heads=128, num_kv_heads=1, max_blk_len=64, total_blk=512)]:
     p = P(**kw)
