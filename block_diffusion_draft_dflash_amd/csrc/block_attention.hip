@@ -1463,6 +1463,7 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
       a.num_pages_m1 = (int32_t)std::min<int64_t>(pg->num_pages - 1, INT32_MAX);
     }
     const int64_t blocks = p.total_blk * p.num_q_heads;
+    if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
     if (p.head_dim == 128)
       hipLaunchKernelGGL(block_attn_f32_kernel<128>, dim3((unsigned)blocks), dim3(64), 0, s, a);
     else
@@ -1532,6 +1533,9 @@ hipError_t launch_block_attention(const dflash_block_attn_params& p, const AttnP
   });
   const int64_t mblocks = (int64_t)p.num_reqs * plan.qtiles * p.num_kv_heads * (QROWS / MROWS);
   const int64_t launch_units = blocks / p.num_kv_heads;
+  // the main grid's unit index (y + 65535 z) is 32-bit, z at most 65535
+  if (!grid_fits(mblocks) || !grid_fits(launch_units) || (launch_units + 65534) / 65535 > 65535)
+    return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)p.num_kv_heads, (unsigned)std::min<int64_t>(launch_units, 65535),
                   (unsigned)((launch_units + 65534) / 65535));
   const dim3 blk(NT), mgrid((unsigned)mblocks);

@@ -447,11 +447,12 @@ hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* w
                              void* ws, hipStream_t s) {
   const int64_t kdim = (int64_t)hkv * dh;
   bf16* wfold = (bf16*)ws;
-  {
-    const int64_t n8 = 2 * kdim * hidden_size / 8;
-    hipLaunchKernelGGL(fold_weights_kernel, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, s,
-                       (const bf16*)wk, (const bf16*)wv, hnw, wfold, kdim, hidden_size);
-  }
+  const int64_t fold_blocks = (2 * kdim * hidden_size / 8 + 255) / 256;
+  const int64_t mtiles = (rows + BM - 1) / BM;
+  const int64_t blocks = (mtiles + 7) / 8 * 8 * (2 * kdim / BN);  // whole groups of 8 row blocks
+  if (!grid_fits(fold_blocks) || !grid_fits(blocks)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(fold_weights_kernel, dim3((unsigned)fold_blocks), dim3(256), 0, s,
+                     (const bf16*)wk, (const bf16*)wv, hnw, wfold, kdim, hidden_size);
 
   CkvArgs a{};
   a.h = (const bf16*)hidden;
@@ -467,8 +468,6 @@ hipError_t launch_context_kv(const void* hidden, const float* hnw, const void* w
   a.hkv = hkv;
   a.max_pos = max_pos;
   a.eps = eps;
-  const int64_t mtiles = (rows + BM - 1) / BM;
-  const int64_t blocks = (mtiles + 7) / 8 * 8 * (a.n / BN);  // whole groups of 8 row blocks
   const size_t lds = kGemmLds;
   static std::once_flag once[64];
   int dev = 0;

@@ -8,6 +8,10 @@
 
 namespace dflash {
 
+// A one-dimensional grid larger than a launch can address is refused
+// (hipErrorInvalidConfiguration) rather than truncated to 32 bits.
+inline bool grid_fits(int64_t blocks) { return blocks >= 0 && blocks <= 0x7fffffff; }
+
 hipError_t launch_rope_table(float* table, int32_t max_pos, int32_t head_dim, double theta,
                              hipStream_t s);
 

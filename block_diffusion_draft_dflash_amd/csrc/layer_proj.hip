@@ -508,6 +508,9 @@ ProjPlan plan_proj(int64_t T, int32_t N, int32_t K, int num_cus, bool allow_wide
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
+// The product's grid (checked by the callers before their first launch).
+bool proj_grid_fits(const ProjPlan& pl) { return grid_fits(pl.mtiles * pl.ntiles * pl.nsplit); }
+
 // W's rows [0, n1) are read from w and rows [n1, N) from w2 (w2 == nullptr: all
 // from w); n1 must be a multiple of the tile width.
 hipError_t launch_proj(const bf16* a, const bf16* w, int64_t T, int32_t N, int32_t K,
@@ -530,6 +533,7 @@ hipError_t launch_proj(const bf16* a, const bf16* w, int64_t T, int32_t N, int32
   g.n1 = w2 ? n1 : N;
   g.ksteps = pl.ksteps; g.nsplit = pl.nsplit; g.part = part; g.out = out;
   const int64_t blocks = pl.mtiles * pl.ntiles * pl.nsplit;
+  if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
   if (pl.bn == 128)
     hipLaunchKernelGGL(proj_gemm_kernel<128>, dim3((unsigned)blocks), dim3(GNT), GemmShape<128>::LDS,
                        s, g);
@@ -562,6 +566,7 @@ hipError_t launch_block_qkv(const void* hidden, void* residual, const float* nor
   bf16* normed = (bf16*)ws;
   const int32_t n = (hq + 2 * hkv) * dh;
   const ProjPlan pl = plan_proj(T, n, hidden_size, num_cus);
+  if (!proj_grid_fits(pl) || !grid_fits(T)) return hipErrorInvalidConfiguration;
   float* part = (float*)((char*)ws + align256((size_t)T * hidden_size * sizeof(bf16)));
   if (residual)
     hipLaunchKernelGGL(residual_norm_kernel<true>, dim3((unsigned)T), dim3(256), 0, s,
@@ -627,13 +632,14 @@ hipError_t launch_context_kv_rows(const void* hidden, const float* hnw, const vo
   if (T == 0) return hipSuccess;
   bf16* normed = (bf16*)ws;
   float* part = (float*)((char*)ws + align256((size_t)T * hidden_size * sizeof(bf16)));
-  hipLaunchKernelGGL(residual_norm_kernel<false>, dim3((unsigned)T), dim3(256), 0, s,
-                     (const bf16*)hidden, (bf16*)nullptr, hnw, normed, hidden_size, eps);
   // K and V in one product over the stacked [W_k; W_v] (columns [0, Hkv Dh) to
   // k_out, the rest to v_out)
   const int32_t n = hkv * dh;
   // (a 128-wide tile must not straddle the two weights)
   const ProjPlan pl = plan_proj(T, 2 * n, hidden_size, num_cus, n % 128 == 0);
+  if (!proj_grid_fits(pl) || !grid_fits(T)) return hipErrorInvalidConfiguration;
+  hipLaunchKernelGGL(residual_norm_kernel<false>, dim3((unsigned)T), dim3(256), 0, s,
+                     (const bf16*)hidden, (bf16*)nullptr, hnw, normed, hidden_size, eps);
   OutSegs o{};
   o.ptr[0] = (bf16*)k_out; o.ptr[1] = o.ptr[2] = (bf16*)v_out;
   o.stride[0] = o.stride[1] = o.stride[2] = n;
@@ -667,9 +673,10 @@ hipError_t launch_fc_combine(const float* aux, const void* w_fc, int64_t T, int3
   const int32_t k = hidden * taps;
   bf16* a = (bf16*)ws;
   const int64_t n8 = T * k / 8;
+  const ProjPlan pl = plan_proj(T, hidden, k, num_cus);
+  if (!proj_grid_fits(pl)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(cast_bf16_kernel, dim3((unsigned)std::min<int64_t>((n8 + 255) / 256, 4096)),
                      dim3(256), 0, s, aux, a, n8);
-  const ProjPlan pl = plan_proj(T, hidden, k, num_cus);
   float* part = (float*)((char*)ws + align256((size_t)T * k * sizeof(bf16)));
   OutSegs o{};
   o.ptr[0] = o.ptr[1] = o.ptr[2] = (bf16*)out;

@@ -160,6 +160,7 @@ hipError_t launch_qknr(T* q, T* k, const float* wq, const float* wk, const int32
   const int64_t per_block = 4 * (64 / (DH / 2 / Piece<T>::N));
   const int64_t blocks = (groups + per_block - 1) / per_block;
   if (blocks == 0) return hipGetLastError();
+  if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL((qk_norm_rope_kernel<T, DH>), dim3((unsigned)blocks), dim3(256), 0, s, q, k,
                      wq, wk, pos, reinterpret_cast<const float2*>(table), max_pos, rows, hq, hkv,
                      eps);
@@ -173,6 +174,7 @@ hipError_t launch_rope_table(float* table, int32_t max_pos, int32_t head_dim, do
   const int32_t half = head_dim / 2;
   const int64_t n = (int64_t)max_pos * half;
   const int64_t blocks = (n + 255) / 256;
+  if (!grid_fits(blocks)) return hipErrorInvalidConfiguration;
   hipLaunchKernelGGL(rope_table_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
                      reinterpret_cast<float2*>(table), max_pos, half, theta);
   return hipGetLastError();

@@ -345,6 +345,33 @@ def test_launch_without_a_device_reports_a_hip_error():
     assert "HIP error" in msg, msg
 
 
+_BIG_GRID_CHILD = r"""
+import ctypes, sys
+sys.path.insert(0, sys.argv[1])
+from block_diffusion_draft_dflash_amd import binding as B
+lib = B.load()
+fake = ctypes.c_void_p(1 << 40)
+# 2^40 rows of 40 heads: more workgroups than one launch addresses
+rc = lib.dflash_qk_norm_rope(B.DFLASH_BF16, fake, fake, fake, fake, fake, 1 << 40, 32, 8, 128,
+                             ctypes.c_float(1e-6), fake, 4096, None)
+print(rc, lib.dflash_last_error().decode())
+"""
+
+
+def test_grid_beyond_one_launch_is_refused():
+    # a grid that would not fit 32 bits is refused before any launch (the
+    # runtime's "invalid configuration" error), never truncated into a launch
+    # that covers part of the rows
+    env = dict(os.environ, HIP_VISIBLE_DEVICES="-1", ROCR_VISIBLE_DEVICES="-1",
+               CUDA_VISIBLE_DEVICES="-1", DFLASH_VALIDATE="0")
+    res = subprocess.run([sys.executable, "-c", _BIG_GRID_CHILD, ROOT], env=env,
+                         capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    rc, _, msg = res.stdout.strip().splitlines()[-1].partition(" ")
+    assert int(rc) == B.DFLASH_ERR_HIP, res.stdout
+    assert "configuration" in msg, msg
+
+
 _TRACE_CHILD = r"""
 import ctypes, sys
 sys.path.insert(0, sys.argv[1])
