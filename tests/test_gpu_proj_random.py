@@ -1,13 +1,14 @@
-"""Seeded random shapes through the projection entry points, each against the
-fp64 oracle at the bounds the fixed-shape tests derive (test_gpu_layer.py for
-dflash_block_qkv and dflash_o_proj, test_gpu_propose.py for dflash_fc_combine
-and dflash_context_kv).
+"""Seeded random shapes through the projection entry points and the standalone
+q/k norm + RoPE, each against the fp64 oracle at the bounds the fixed-shape
+tests derive (test_gpu_layer.py for dflash_block_qkv and dflash_o_proj,
+test_gpu_propose.py for dflash_fc_combine and dflash_context_kv,
+test_gpu_parity.py's one-rounding bound for dflash_qk_norm_rope).
 
 Row counts, hidden sizes, head geometries and the residual are drawn per case,
 so the planner's branches (128- and 64-wide column tiles, uneven and
 power-of-two K splits, a single slice, the few-row and the large-row context
 forms, partial row tiles) all meet the oracle. The kind of call cycles with
-the case number; DFLASH_RANDOM_CASES=N runs the first N seeds (16 by default).
+the case number; DFLASH_RANDOM_CASES=N runs the first N seeds (20 by default).
 """
 import os
 
@@ -23,8 +24,8 @@ from test_gpu_propose import _context_kv_vs_oracle
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = int(os.environ.get("DFLASH_RANDOM_CASES", "16"))
-KINDS = ("block_qkv", "o_proj", "fc_combine", "context_kv")
+N_CASES = int(os.environ.get("DFLASH_RANDOM_CASES", "20"))
+KINDS = ("block_qkv", "o_proj", "fc_combine", "context_kv", "qk_norm_rope")
 
 
 def _bits(rng, shape, scale):
@@ -108,10 +109,50 @@ def _context_kv(rng, tag):
     _context_kv_vs_oracle(rows, hkv, h)
 
 
+def _qk_norm_rope(rng, tag):
+    # head counts that leave partial chunks of the kernel's 8-head lane groups,
+    # the K-only form, both dtypes, and positions past either end of the table
+    # (the call clamps them into it)
+    from oracle import dflash_oracle as O
+    t = int(rng.integers(1, 3001))
+    hkv = int(rng.choice([1, 2, 3, 4, 8, 16]))
+    hq = hkv * int(rng.choice([1, 2, 4, 5, 8])) if rng.random() < 0.8 else 0
+    dh = int(rng.choice([64, 128]))
+    f32 = bool(rng.random() < 0.3)
+    max_pos = int(rng.integers(1, 50001))
+    print(f"case {tag}: T={t} Hq={hq} Hkv={hkv} Dh={dh} {'f32' if f32 else 'bf16'} max_pos={max_pos}",
+          flush=True)
+    dev = "cuda"
+    pos = rng.integers(-50, max_pos + 50, size=t).astype(np.int32)
+    rnd = (lambda x: x.astype(np.float32)) if f32 else \
+        (lambda x: bf16_bits_to_f32(f32_to_bf16_bits(x.astype(np.float32))))
+    k = rnd(rng.standard_normal((t, hkv, dh)))
+    q = rnd(rng.standard_normal((t, hq, dh))) if hq else None
+    kw = bf16_bits_to_f32(f32_to_bf16_bits(rng.uniform(0.5, 1.5, dh).astype(np.float32)))
+    qw = bf16_bits_to_f32(f32_to_bf16_bits(rng.uniform(0.5, 1.5, dh).astype(np.float32)))
+    dt = torch.float32 if f32 else torch.bfloat16
+    kd = torch.from_numpy(k).to(dev).to(dt)
+    qd = torch.from_numpy(q).to(dev).to(dt) if hq else None
+    table = torch.empty((max_pos, dh // 2, 2), dtype=torch.float32, device=dev)
+    B.dflash_rope_table(table, max_pos, dh, 1e6)
+    B.dflash_qk_norm_rope(qd, kd, torch.from_numpy(qw).to(dev) if hq else None, torch.from_numpy(kw).to(dev),
+                          torch.from_numpy(pos).to(dev), 1e-6, table)
+    torch.cuda.synchronize()
+    eff = np.clip(pos, 0, max_pos - 1)
+    qo, ko = O.qk_norm_rope(q.astype(np.float64) if hq else None, k.astype(np.float64), qw, kw, eff, 1e-6, 1e6)
+    rel = 1e-6 if f32 else 2.0 ** -7
+    for name, g, o in (("k", kd, ko), ("q", qd, qo)):
+        if g is None:
+            continue
+        err = np.abs(to_host_f64(g) - o)
+        print(f"[{tag} {name}] max abs {err.max():.3e}", flush=True)
+        assert (err <= rel * np.abs(o) + 1e-5).all(), f"{tag} {name}: beyond the one-rounding bound"
+
+
 @pytest.mark.parametrize("i", range(N_CASES))
 def test_random_projection_shape(i):
     rng = np.random.default_rng(9100 + i)
     kind = KINDS[i % len(KINDS)]
     fn = {"block_qkv": _block_qkv, "o_proj": _o_proj, "fc_combine": _fc_combine,
-          "context_kv": _context_kv}[kind]
+          "context_kv": _context_kv, "qk_norm_rope": _qk_norm_rope}[kind]
     fn(rng, f"random {i} {kind}")
